@@ -1,0 +1,201 @@
+"""CPU oracle of the block-wise FP8 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The product library
+(``block_scaled_fp8_x128_amd``) never imports it, and it never imports the
+product library: the two share no code.  Inputs come from ``synth``.
+
+This module is argument marshalling (numpy <-> ctypes) around the plain C
+definitions in ``fp8bs_oracle.c``; every arithmetic step lives there, with
+the passage of the article each one follows.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "fp8bs_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+SCALE_EXACT = 0
+SCALE_POW2 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP, no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
+               "-Wall", "-Wextra", "-shared", "-fPIC", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint32]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint32
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode_array.argtypes = [P, I64, P]
+        L.oracle_e4m3_decode_array.argtypes = [P, I64, P]
+        L.oracle_block_scale.restype = ctypes.c_float
+        L.oracle_block_scale.argtypes = [ctypes.c_float, ctypes.c_int]
+        L.oracle_quant_act_1x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
+        L.oracle_quant_w_128x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
+        L.oracle_gemm.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_gemm_sampled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
+        L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+        L.oracle_grouped_gemm_sampled.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P, I64, P]
+        L.oracle_max_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError("expected %s, got %s" % (np.dtype(dtype), a.dtype))
+    return a
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+# ---- E4M3 codec ----------------------------------------------------------------
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(v)))
+
+
+def e4m3_encode_array(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_decode_array(c) -> np.ndarray:
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def block_scale(amax: float, mode: int = SCALE_EXACT) -> float:
+    """fp32 dequantization scale of a block with largest magnitude ``amax``."""
+    return float(lib().oracle_block_scale(float(amax), int(mode)))
+
+
+# ---- quantizers ----------------------------------------------------------------
+
+def quant_act_1x128(x_bf16, mode: int = SCALE_EXACT):
+    """x_bf16: uint16 [M, K] -> (codes uint8 [M, K], scales fp32 [M, K/128])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // 128), dtype=np.float32)
+    lib().oracle_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), int(mode))
+    return q, s
+
+
+def quant_w_128x128(w_bf16, mode: int = SCALE_EXACT):
+    """w_bf16: uint16 [N, K] -> (codes uint8 [N, K], scales fp32 [N/128, K/128])."""
+    w = _c(w_bf16, np.uint16)
+    N, K = w.shape
+    if N % 128 or K % 128:
+        raise ValueError("N and K must be multiples of 128")
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty((N // 128, K // 128), dtype=np.float32)
+    lib().oracle_quant_w_128x128(_ptr(w), N, K, _ptr(q), _ptr(s), int(mode))
+    return q, s
+
+
+# ---- GEMMs ---------------------------------------------------------------------
+
+def gemm(xq, xs, wq, ws) -> np.ndarray:
+    """fp64 Y [M, N] = block-scaled Xq Wq^T."""
+    xq = _c(xq, np.uint8)
+    wq = _c(wq, np.uint8)
+    xs = _c(xs, np.float32)
+    ws = _c(ws, np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y))
+    return y
+
+
+def gemm_sampled(xq, xs, wq, ws, rows, cols) -> np.ndarray:
+    xq = _c(xq, np.uint8)
+    wq = _c(wq, np.uint8)
+    xs = _c(xs, np.float32)
+    ws = _c(ws, np.float32)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty(rows.shape, dtype=np.float64)
+    lib().oracle_gemm_sampled(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
+                              _ptr(rows), _ptr(cols), rows.size, _ptr(y))
+    return y
+
+
+def grouped_gemm(xq, xs, wq, ws, offsets) -> np.ndarray:
+    """fp64 Y [M_total, N]; wq [E, N, K], ws [E, N/128, K/128], offsets int32 [E+1]."""
+    xq = _c(xq, np.uint8)
+    wq = _c(wq, np.uint8)
+    xs = _c(xs, np.float32)
+    ws = _c(ws, np.float32)
+    offs = _c(np.asarray(offsets, dtype=np.int32), np.int32)
+    M, K = xq.shape
+    E, N, _ = wq.shape
+    y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_grouped_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offs), E, M, N, K, _ptr(y))
+    return y
+
+
+def grouped_gemm_sampled(xq, xs, wq, ws, offsets, rows, cols) -> np.ndarray:
+    xq = _c(xq, np.uint8)
+    wq = _c(wq, np.uint8)
+    xs = _c(xs, np.float32)
+    ws = _c(ws, np.float32)
+    offs = _c(np.asarray(offsets, dtype=np.int32), np.int32)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    M, K = xq.shape
+    E, N, _ = wq.shape
+    y = np.empty(rows.shape, dtype=np.float64)
+    lib().oracle_grouped_gemm_sampled(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offs), E, M, N, K,
+                                      _ptr(rows), _ptr(cols), rows.size, _ptr(y))
+    return y

@@ -1,0 +1,133 @@
+"""Pins of the oracle's block-scaled GEMM and grouped (MoE) GEMM.
+
+The article ("NVIDIA NeMo RL achieves 48% speedup with end-to-end FP8 precision
+training", section "Technical breakthrough") says linear layers run FP8 math on
+the block-quantized operands; the MoE form follows its Qwen3-30B (mixture of
+experts) result in section "Real-world performance gains".  The oracle sums
+each 128-wide K block exactly and applies the two fp32 scales per block; the
+tests tie that to the closed form (an fp64 matmul of the dequantized operands),
+to exact integer matmuls and to the per-expert decomposition.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+
+
+def _dequant_rows(orc, q, s):
+    """decode(q) * s with s broadcast over 1x128 blocks (activation layout)."""
+    d = orc.e4m3_decode_array(q)
+    return d * np.repeat(s.astype(np.float64), 128, axis=1)
+
+
+def _dequant_tiles(orc, q, s):
+    """decode(q) * s with s broadcast over 128x128 blocks (weight layout)."""
+    d = orc.e4m3_decode_array(q)
+    return d * np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1)
+
+
+def _operands(orc, M, N, K, seed, mode=0):
+    x = synth.activations(M, K, seed=seed)
+    w = synth.weights(N, K, seed=seed, sub=synth.SUB_W)
+    xq, xs = orc.quant_act_1x128(x, mode)
+    wq, ws = orc.quant_w_128x128(w, mode)
+    return xq, xs, wq, ws
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 512), (256, 256, 512), (200, 384, 640), (1, 128, 128), (130, 256, 1024)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_equals_matmul_of_dequantized(orc, shape, mode):
+    M, N, K = shape
+    xq, xs, wq, ws = _operands(orc, M, N, K, seed=M + N + K, mode=mode)
+    y = orc.gemm(xq, xs, wq, ws)
+    ref = _dequant_rows(orc, xq, xs) @ _dequant_tiles(orc, wq, ws).T
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert rms > 0
+    assert np.max(np.abs(y - ref)) <= 1e-12 * rms * np.sqrt(K)
+    # the same closed form with the operand order swapped is a different matrix
+    if M == N:
+        assert np.max(np.abs(y - ref.T)) > 1e-3 * rms
+
+
+def test_gemm_integer_special_case(orc):
+    """All scales 1 and codes of small integers: Y is an exact integer matmul."""
+    g = np.random.default_rng(5)
+    # codes of the integers 0..8 and their negatives: 0x00 0x38 0x40 0x44 0x48 0x4A 0x4C 0x4E 0x50
+    int_codes = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50], dtype=np.uint8)
+    M, N, K = 64, 128, 384
+    ix = g.integers(0, 9, (M, K))
+    iw = g.integers(0, 9, (N, K))
+    sx = g.integers(0, 2, (M, K))
+    sw = g.integers(0, 2, (N, K))
+    xq = int_codes[ix] | (sx * 0x80).astype(np.uint8)
+    wq = int_codes[iw] | (sw * 0x80).astype(np.uint8)
+    vx = ix * (1 - 2 * sx)
+    vw = iw * (1 - 2 * sw)
+    y = orc.gemm(xq, np.ones((M, K // 128), np.float32), wq, np.ones((N // 128, K // 128), np.float32))
+    assert np.array_equal(y, (vx @ vw.T).astype(np.float64))
+
+
+def test_gemm_single_block_is_scaled_dot(orc):
+    """K = 128: Y = xs * ws * P with P the exact dot product of the decoded codes."""
+    xq, xs, wq, ws = _operands(orc, 16, 256, 128, seed=3)
+    y = orc.gemm(xq, xs, wq, ws)
+    P = orc.e4m3_decode_array(xq) @ orc.e4m3_decode_array(wq).T  # exact: 2^-18 grid, < 2^43
+    ref = (xs.astype(np.float64) @ np.ones((1, 256))) * np.repeat(ws[:, 0].astype(np.float64), 128)[None, :] * P
+    assert np.array_equal(y, ref)
+
+
+def test_gemm_sampled_equals_full(orc):
+    xq, xs, wq, ws = _operands(orc, 96, 256, 384, seed=4)
+    y = orc.gemm(xq, xs, wq, ws)
+    g = np.random.default_rng(1)
+    rows = g.integers(0, 96, 500)
+    cols = g.integers(0, 256, 500)
+    assert np.array_equal(orc.gemm_sampled(xq, xs, wq, ws, rows, cols), y[rows, cols])
+
+
+def _grouped_operands(orc, counts, N, K, seed, mode=0):
+    offs = synth.offsets_from_counts(counts)
+    M = int(offs[-1])
+    E = len(counts)
+    x = synth.activations(max(M, 1), K, seed=seed)[:M]
+    w = synth.expert_weights(E, N, K, seed=seed)
+    xq, xs = orc.quant_act_1x128(x, mode)
+    wq = np.empty((E, N, K), np.uint8)
+    ws = np.empty((E, N // 128, K // 128), np.float32)
+    for e in range(E):
+        wq[e], ws[e] = orc.quant_w_128x128(w[e], mode)
+    return xq, xs, wq, ws, offs
+
+
+@pytest.mark.parametrize("counts", [[5, 0, 129, 1, 64], [0, 0, 3], [128, 128], [0]])
+def test_grouped_equals_per_expert_gemms(orc, counts):
+    N, K = 256, 384
+    xq, xs, wq, ws, offs = _grouped_operands(orc, counts, N, K, seed=len(counts))
+    y = orc.grouped_gemm(xq, xs, wq, ws, offs)
+    assert y.shape == (sum(counts), N)
+    for e in range(len(counts)):
+        a, b = offs[e], offs[e + 1]
+        if b > a:
+            ref = _dequant_rows(orc, xq[a:b], xs[a:b]) @ _dequant_tiles(orc, wq[e], ws[e]).T
+            rms = np.sqrt(np.mean(ref ** 2))
+            assert np.max(np.abs(y[a:b] - ref)) <= 1e-12 * rms * np.sqrt(K)
+            assert np.array_equal(y[a:b], orc.gemm(xq[a:b], xs[a:b], wq[e], ws[e]))
+    if y.size:
+        g = np.random.default_rng(2)
+        rows = g.integers(0, y.shape[0], 200)
+        cols = g.integers(0, N, 200)
+        assert np.array_equal(orc.grouped_gemm_sampled(xq, xs, wq, ws, offs, rows, cols), y[rows, cols])
+
+
+def test_routing_counts():
+    row_token, offs = synth.moe_routing(8192, 128, 8, seed=0)
+    assert offs[0] == 0 and offs[-1] == 65536 and row_token.size == 65536
+    counts = np.diff(offs)
+    assert (counts >= 0).all()
+    # each token appears exactly top-k times
+    assert (np.bincount(row_token, minlength=8192) == 8).all()
+    # rows are ordered by token inside each expert group
+    for e in range(0, 128, 17):
+        seg = row_token[offs[e]:offs[e + 1]]
+        assert (np.diff(seg) > 0).all()
