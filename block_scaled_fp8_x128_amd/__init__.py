@@ -1,0 +1,242 @@
+"""Block-scaled FP8 linear layers for AMD MI355X (gfx950).
+
+Thin Python binding of ``libfp8bs.so`` (C ABI in ``include/fp8bs.h``): each
+function checks dtypes, shapes and devices, allocates outputs with torch (torch
+is used for device memory and streams only) and passes raw pointers plus the
+current HIP stream.  Every arithmetic step runs in the library's kernels; there
+is no fallback: if the library is not built, loading it raises.
+
+Method: the article "NVIDIA NeMo RL achieves 48% speedup with end-to-end FP8
+precision training" (Jessie A Ellis, Apr 20 2026), section "Technical
+breakthrough" -- block-wise E4M3 with 1x128 activation blocks and 128x128
+weight blocks, FP8 math in linear layers; section "Real-world performance
+gains" -- scales recalibrated after every step, MoE models; closing section --
+power-of-2 scaling factors.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8bs.so")
+
+SCALE_EXACT = 0
+SCALE_POW2 = 1
+OUT_BF16 = 0
+OUT_FP32 = 1
+
+# The functions declared in include/fp8bs.h, in declaration order.
+EXPORTS = (
+    "quant_act_1x128",
+    "quant_w_128x128",
+    "quant_w_128x128_batched",
+    "fp8_block_gemm",
+    "fp8_block_grouped_gemm",
+    "fp8bs_gemm_workspace_size",
+    "fp8bs_grouped_workspace_size",
+    "fp8bs_status_string",
+    "fp8bs_abi_version",
+)
+
+_lib = None
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed with status %d: %s" % (fn, status, status_string(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp8bs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libfp8bs.so is not built (run `python -m block_scaled_fp8_x128_amd.build`)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.quant_act_1x128.argtypes = [P, I64, I64, P, P, I32, P]
+        L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
+        L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
+        L.fp8_block_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
+        L.fp8_block_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P, SZ, P]
+        L.fp8bs_gemm_workspace_size.argtypes = [I64, I64, I64]
+        L.fp8bs_gemm_workspace_size.restype = SZ
+        L.fp8bs_grouped_workspace_size.argtypes = [I64, I64, I64, I64]
+        L.fp8bs_grouped_workspace_size.restype = SZ
+        L.fp8bs_status_string.argtypes = [I32]
+        L.fp8bs_status_string.restype = ctypes.c_char_p
+        L.fp8bs_abi_version.restype = I32
+        for fn in ("quant_act_1x128", "quant_w_128x128", "quant_w_128x128_batched", "fp8_block_gemm",
+                   "fp8_block_grouped_gemm"):
+            getattr(L, fn).restype = I32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8bs_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().fp8bs_abi_version())
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Fp8bsError(fn, status)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _bf16_payload(x: torch.Tensor, name: str) -> torch.Tensor:
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("%s must be bfloat16 (or its 16-bit payload), got %s" % (name, x.dtype))
+    if not x.is_cuda:
+        raise ValueError("%s must be on a HIP device" % name)
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return x
+
+
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("%s must hold E4M3 codes (uint8 or float8_e4m3fn), got %s" % (name, t.dtype))
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+    return t
+
+
+def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 device tensor" % name)
+    return t
+
+
+# ---- quantizers ----------------------------------------------------------------
+
+def quant_act_1x128(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 [M, K] -> (codes uint8 [M, K], scales fp32 [M, K/128])."""
+    x = _bf16_payload(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        xs = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    else:
+        xq, xs = out
+    _check("quant_act_1x128", lib().quant_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(xs), int(mode), _stream(x)))
+    return xq, xs
+
+
+def quant_w_128x128(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 [N, K] -> (codes uint8 [N, K], scales fp32 [N/128, K/128])."""
+    w = _bf16_payload(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if out is None:
+        wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+        ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    else:
+        wq, ws = out
+    _check("quant_w_128x128", lib().quant_w_128x128(_ptr(w), N, K, _ptr(wq), _ptr(ws), int(mode), _stream(w)))
+    return wq, ws
+
+
+def quant_w_128x128_batched(ws_in: Sequence[torch.Tensor], mode: int = SCALE_EXACT, outs=None):
+    """Re-quantize many weight tensors in one call (per-step recalibration)."""
+    n = len(ws_in)
+    if n == 0:
+        return []
+    tensors = [_bf16_payload(w, "w[%d]" % i) for i, w in enumerate(ws_in)]
+    if outs is None:
+        outs = [(torch.empty(w.shape, dtype=torch.uint8, device=w.device),
+                 torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32, device=w.device))
+                for w in tensors]
+    arr_p = ctypes.c_void_p * n
+    arr_i = ctypes.c_int64 * n
+    wp = arr_p(*[w.data_ptr() for w in tensors])
+    Ns = arr_i(*[w.shape[0] for w in tensors])
+    Ks = arr_i(*[w.shape[1] for w in tensors])
+    qp = arr_p(*[o[0].data_ptr() for o in outs])
+    sp = arr_p(*[o[1].data_ptr() for o in outs])
+    st = lib().quant_w_128x128_batched(n, ctypes.cast(wp, ctypes.c_void_p), ctypes.cast(Ns, ctypes.c_void_p),
+                                       ctypes.cast(Ks, ctypes.c_void_p), ctypes.cast(qp, ctypes.c_void_p),
+                                       ctypes.cast(sp, ctypes.c_void_p), int(mode), _stream(tensors[0]))
+    _check("quant_w_128x128_batched", st)
+    return outs
+
+
+# ---- GEMMs ---------------------------------------------------------------------
+
+def _out_code(out_dtype) -> int:
+    if out_dtype in (torch.bfloat16, OUT_BF16):
+        return OUT_BF16
+    if out_dtype in (torch.float32, OUT_FP32):
+        return OUT_FP32
+    raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().fp8bs_gemm_workspace_size(M, N, K))
+
+
+def grouped_workspace_size(E: int, M_total: int, N: int, K: int) -> int:
+    return int(lib().fp8bs_grouped_workspace_size(E, M_total, N, K))
+
+
+def fp8_block_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """Y [M, N] = dequant(xq, xs) @ dequant(wq, ws)^T."""
+    xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
+    xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or xs.shape != (M, K // 128) or ws.shape != (N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=xq.device)
+    need = gemm_workspace_size(M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_block_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code,
+                              _ptr(workspace), wsz, _stream(xq))
+    _check("fp8_block_gemm", st)
+    return out
+
+
+def fp8_block_grouped_gemm(xq, xs, wq, ws, group_offsets, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """Y [M_total, N]: rows offs[e]..offs[e+1]-1 multiplied by expert e's weights."""
+    xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
+    xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
+    if group_offsets.dtype != torch.int32 or not group_offsets.is_cuda:
+        raise ValueError("group_offsets must be an int32 device tensor")
+    M, K = xq.shape
+    E, N, K2 = wq.shape
+    if K2 != K or xs.shape != (M, K // 128) or ws.shape != (E, N // 128, K // 128) or group_offsets.numel() != E + 1:
+        raise ValueError("operand shapes do not match")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=xq.device)
+    need = grouped_workspace_size(E, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_block_grouped_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(group_offsets), E, M, N, K,
+                                      _ptr(out), code, _ptr(workspace), wsz, _stream(xq))
+    _check("fp8_block_grouped_gemm", st)
+    return out

@@ -1,0 +1,231 @@
+// fp8bs_abi.hip -- the extern "C" boundary declared in include/fp8bs.h.
+//
+// Checks every argument before touching the device, verifies once per device
+// that it is a gfx950, and hands over to the kernel launchers.  Nothing here
+// allocates, synchronizes or throws.
+#include <atomic>
+#include <string.h>
+
+#include "fp8bs.h"
+#include "fp8bs_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not yet queried, 1 = gfx950, 2 = other device
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return FP8BS_UNSUPPORTED_DEVICE;
+    if (dev < kMaxDevices) {
+        const int k = g_device_kind[dev].load(std::memory_order_relaxed);
+        if (k != 0)
+            return k == 1 ? FP8BS_OK : FP8BS_UNSUPPORTED_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return FP8BS_UNSUPPORTED_DEVICE;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices)
+        g_device_kind[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? FP8BS_OK : FP8BS_UNSUPPORTED_DEVICE;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// A device tensor argument: null is allowed only when it holds no element.
+bool tensor_ok(const void *p, int64_t elems, size_t align)
+{
+    if (elems == 0)
+        return true;
+    return p != nullptr && aligned(p, align);
+}
+
+// Largest extent any kernel indexes with 32-bit tile counters.
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+int status_of(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_HIP_ERROR; }
+
+int check_quant(const void *x, int64_t R, int64_t K, const void *q, const float *s, int mode, bool rows_blocked)
+{
+    if (R < 0 || K <= 0 || (mode != FP8BS_SCALE_EXACT && mode != FP8BS_SCALE_POW2))
+        return FP8BS_INVALID_ARG;
+    if (K % 128 != 0 || (rows_blocked && R % 128 != 0))
+        return FP8BS_UNSUPPORTED_SHAPE;
+    // grid sizes stay below 2^31 workgroups: activation blocks / 64, weight blocks
+    if (R >= kMaxDim || K >= kMaxDim || R * (K / 128) >= kMaxDim * 64 || (R / 128) * (K / 128) >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    const int64_t n = R * K;
+    if (!tensor_ok(x, n, 16) || !tensor_ok(q, n, 16) || !tensor_ok(s, n, 4))
+        return FP8BS_INVALID_ARG;
+    return FP8BS_OK;
+}
+
+int check_gemm_common(const void *xq, const float *xs, const void *y, int64_t M, int64_t N, int64_t K, int out_dtype)
+{
+    if (M < 0 || N <= 0 || K <= 0 || (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_FP32))
+        return FP8BS_INVALID_ARG;
+    if (N % 128 != 0 || K % 128 != 0)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (!tensor_ok(xq, M * K, 16) || !tensor_ok(xs, M * K, 4) || !tensor_ok(y, M * N, 16))
+        return FP8BS_INVALID_ARG;
+    return FP8BS_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
+
+const char *fp8bs_status_string(int status)
+{
+    switch (status) {
+    case FP8BS_OK:
+        return "ok";
+    case FP8BS_INVALID_ARG:
+        return "invalid argument (null or misaligned pointer, negative size, unknown enum value)";
+    case FP8BS_UNSUPPORTED_SHAPE:
+        return "unsupported shape (K, or N where required, not a multiple of 128, or too large)";
+    case FP8BS_UNSUPPORTED_DEVICE:
+        return "unsupported device (the current HIP device is not a gfx950)";
+    case FP8BS_WORKSPACE_TOO_SMALL:
+        return "workspace too small";
+    case FP8BS_HIP_ERROR:
+        return "HIP runtime error at launch";
+    default:
+        return "unknown status";
+    }
+}
+
+int quant_act_1x128(const void *x_bf16, int64_t M, int64_t K, void *xq, float *xs, int scale_mode, void *stream)
+{
+    int st = check_quant(x_bf16, M, K, xq, xs, scale_mode, false);
+    if (st != FP8BS_OK)
+        return st;
+    if (M == 0)
+        return FP8BS_OK;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_quant_act(x_bf16, M, K, xq, xs, scale_mode, (hipStream_t)stream));
+}
+
+int quant_w_128x128(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, int scale_mode, void *stream)
+{
+    int st = check_quant(w_bf16, N, K, wq, ws, scale_mode, true);
+    if (st != FP8BS_OK)
+        return st;
+    if (N == 0)
+        return FP8BS_OK;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    fp8bs::WTensor t = {w_bf16, wq, ws, N, K};
+    return status_of(fp8bs::launch_quant_w(&t, 1, scale_mode, (hipStream_t)stream));
+}
+
+int quant_w_128x128_batched(int64_t count, const void *const *w_bf16, const int64_t *N, const int64_t *K,
+                            void *const *wq, float *const *ws, int scale_mode, void *stream)
+{
+    if (count < 0)
+        return FP8BS_INVALID_ARG;
+    if (count == 0)
+        return FP8BS_OK;
+    if (!w_bf16 || !N || !K || !wq || !ws)
+        return FP8BS_INVALID_ARG;
+    bool any = false;
+    for (int64_t i = 0; i < count; ++i) {
+        const int st = check_quant(w_bf16[i], N[i], K[i], wq[i], ws[i], scale_mode, true);
+        if (st != FP8BS_OK)
+            return st;
+        any = any || N[i] > 0;
+    }
+    if (!any)
+        return FP8BS_OK;
+    int st = check_device();
+    if (st != FP8BS_OK)
+        return st;
+    // pack the non-empty tensors, in order, a fixed-size batch at a time
+    fp8bs::WTensor buf[64];
+    int64_t n = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        if (N[i] == 0)
+            continue;
+        buf[n++] = fp8bs::WTensor{w_bf16[i], wq[i], ws[i], N[i], K[i]};
+        if (n == 64) {
+            if (fp8bs::launch_quant_w(buf, n, scale_mode, (hipStream_t)stream) != hipSuccess)
+                return FP8BS_HIP_ERROR;
+            n = 0;
+        }
+    }
+    if (n > 0 && fp8bs::launch_quant_w(buf, n, scale_mode, (hipStream_t)stream) != hipSuccess)
+        return FP8BS_HIP_ERROR;
+    return FP8BS_OK;
+}
+
+size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    return fp8bs::gemm_workspace_size(M, N, K);
+}
+
+size_t fp8bs_grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K)
+{
+    (void)E;
+    (void)M_total;
+    (void)N;
+    (void)K;
+    return 0;
+}
+
+int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+                   void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = check_gemm_common(xq, xs, y, M, N, K, out_dtype);
+    if (st != FP8BS_OK)
+        return st;
+    if (!tensor_ok(wq, N * K, 16) || !tensor_ok(ws, N * K, 4))
+        return FP8BS_INVALID_ARG;
+    if (M == 0)
+        return FP8BS_OK;
+    const size_t need = fp8bs::gemm_workspace_size(M, N, K);
+    if (workspace_bytes < need)
+        return FP8BS_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+        return FP8BS_INVALID_ARG;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_gemm(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, workspace,
+                                        (hipStream_t)stream));
+}
+
+int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                           const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
+                           int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    int st = check_gemm_common(xq, xs, y, M_total, N, K, out_dtype);
+    if (st != FP8BS_OK)
+        return st;
+    if (E < 0 || (E == 0 && M_total > 0) || E >= kMaxDim)
+        return FP8BS_INVALID_ARG;
+    if (M_total == 0)
+        return FP8BS_OK;
+    if (!tensor_ok(wq, E * N * K, 16) || !tensor_ok(ws, E * N * K, 4) || group_offsets == nullptr ||
+        !aligned(group_offsets, 4))
+        return FP8BS_INVALID_ARG;
+    if ((M_total + 127) / 128 + E >= kMaxDim / (N / 128))
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_grouped_gemm(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y,
+                                                out_dtype == FP8BS_OUT_FP32, (hipStream_t)stream));
+}
+
+} // extern "C"

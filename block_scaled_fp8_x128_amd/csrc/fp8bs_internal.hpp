@@ -1,0 +1,54 @@
+// fp8bs_internal.hpp -- host-side launchers shared between the kernel files
+// and the C ABI layer.  Every launcher enqueues on `stream` and returns the
+// HIP status of the launch; argument checking happens in the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <tuple>
+#include <utility>
+
+namespace fp8bs {
+
+// Launch through hipLaunchKernel so that the status of THIS launch is
+// returned (the <<<>>> form reports through hipGetLastError, which would also
+// pick up an unrelated earlier error of the caller).
+template <typename... KArgs, typename... Args>
+static inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                                Args... args)
+{
+    std::tuple<KArgs...> held(static_cast<KArgs>(args)...);
+    void *ptrs[sizeof...(KArgs)];
+    std::apply([&](auto &...a) {
+        int i = 0;
+        ((ptrs[i++] = (void *)&a), ...);
+    }, held);
+    return hipLaunchKernel((const void *)kern, grid, block, ptrs, shmem, stream);
+}
+
+// ---- quantizers (fp8bs_quant.hip) ------------------------------------------
+
+hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float *xs, int mode, hipStream_t stream);
+
+// One weight tensor of a batched weight quantization.
+struct WTensor {
+    const void *w;
+    void *q;
+    float *s;
+    int64_t N, K;
+};
+// Quantizes `count` tensors (count >= 1, every N, K a positive multiple of
+// 128) in as few launches as the kernel-argument budget allows.
+hipError_t launch_quant_w(const WTensor *t, int64_t count, int mode, hipStream_t stream);
+
+// ---- GEMMs (fp8bs_gemm.hip) --------------------------------------------------
+
+size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                       int64_t K, void *y, int out_fp32, void *workspace, hipStream_t stream);
+hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                               const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
+                               int out_fp32, hipStream_t stream);
+
+} // namespace fp8bs

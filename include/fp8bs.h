@@ -1,0 +1,190 @@
+/*
+ * fp8bs.h -- C ABI of the block-scaled FP8 linear-layer library for AMD
+ * Instinct MI355X (gfx950, CDNA4).
+ *
+ * The method: the article "NVIDIA NeMo RL achieves 48% speedup with end-to-end
+ * FP8 precision training" (Jessie A Ellis, Apr 20 2026; mexc.co/hi-IN/news/
+ * 1041474 and its two translations).  Its section "Technical breakthrough"
+ * quantizes block-wise to FP8 E4M3 -- one block of 128x128 for weights, 1x128
+ * for activations -- and runs the linear layers in FP8 math.  Its section
+ * "Real-world performance gains" recalibrates the quantization scales after
+ * every training step and reports a matching accuracy on a mixture-of-experts
+ * model.  Its closing section offers power-of-2 scaling factors.  The article
+ * prints no formula: the scale rule (amax / 448), the rounding (saturating
+ * round-to-nearest-even of the correctly rounded fp32 quotient), fp32 scales
+ * applied per 128-wide K block, and the grouped MoE form are this library's
+ * statement of the method.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *   allocates nothing.  Tensors are dense and row-major.
+ * - bf16 tensors are passed as raw 16-bit payloads.  FP8 codes are bytes in
+ *   the OCP E4M3FN encoding (bias 7, largest finite 448, NaN = S.1111.111).
+ * - Scales are fp32 DEQUANTIZATION multipliers: x ~= decode(q) * s.
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *   null stream).  The library never synchronizes; results are ready when the
+ *   stream reaches them.  Calls are reentrant; repeated calls with the same
+ *   arguments produce bit-identical results (no atomics in any reduction).
+ * - Return value: FP8BS_OK (0) or one of the status codes below.  Arguments
+ *   are checked before any device work is enqueued, so a non-zero return
+ *   means nothing was launched, except FP8BS_HIP_ERROR, which reports a
+ *   failed launch.  No C++ exception and no abort crosses this boundary.
+ * - M == 0 (or M_total == 0) is a valid no-op.  K and N must be multiples of
+ *   128.  Tensor pointers must be 16-byte aligned, scale pointers 4-byte
+ *   aligned.  Non-finite inputs are outside the contract: the output is then
+ *   unspecified, but no kernel reads or writes out of bounds.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BS_ABI_VERSION 1
+
+/* Symbols of this header are the only ones the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define FP8BS_API __attribute__((visibility("default")))
+#else
+#define FP8BS_API
+#endif
+
+enum fp8bs_status {
+    FP8BS_OK = 0,
+    FP8BS_INVALID_ARG = 1,         /* null pointer with a non-zero extent, negative size, misaligned
+                                      pointer, unknown enum value */
+    FP8BS_UNSUPPORTED_SHAPE = 2,   /* K (or N where required) not a multiple of 128; size too large */
+    FP8BS_UNSUPPORTED_DEVICE = 3,  /* the current HIP device is not a gfx950 */
+    FP8BS_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the size the query function returns */
+    FP8BS_HIP_ERROR = 5            /* the HIP runtime refused a launch */
+};
+
+/* scale_mode */
+enum fp8bs_scale_mode {
+    FP8BS_SCALE_EXACT = 0, /* s = RN_fp32(amax / 448); the largest element maps to +-448 */
+    FP8BS_SCALE_POW2 = 1   /* s = 2^k, the least k with amax <= 448 * 2^k (never clips) */
+};
+
+/* out_dtype */
+enum fp8bs_out_dtype {
+    FP8BS_OUT_BF16 = 0, /* bf16 payloads, round-to-nearest-even of the fp32 result */
+    FP8BS_OUT_FP32 = 1  /* the fp32 accumulator itself */
+};
+
+/*
+ * quant_act_1x128 -- activation quantizer, one scale per 1x128 row block
+ * (article section "Technical breakthrough": 1x128 granularity for
+ * activations).
+ *
+ *   x_bf16 : [M, K] bf16 payloads (input, read only)
+ *   xq     : [M, K] E4M3 codes (output)
+ *   xs     : [M, K/128] fp32 scales (output); xs[m, kb] covers
+ *            x[m, 128*kb .. 128*kb+127]
+ *
+ * For each block: amax = max |x| (exact); s = scale(amax, scale_mode), with
+ * s = 1 for an all-zero block; q = E4M3_sat_RNE(RN_fp32(x / s)), the sign of
+ * x (also of -0) kept in the code.  Bit-exact and deterministic.
+ * Errors: INVALID_ARG (null x/xq/xs with M > 0, M < 0, K <= 0, misalignment,
+ * bad scale_mode), UNSUPPORTED_SHAPE (K % 128 != 0), UNSUPPORTED_DEVICE.
+ */
+FP8BS_API int quant_act_1x128(const void *x_bf16, int64_t M, int64_t K, void *xq, float *xs, int scale_mode,
+                    void *stream);
+
+/*
+ * quant_w_128x128 -- weight quantizer, one scale per 128x128 block (article
+ * section "Technical breakthrough": 128x128 granularity for weights).  Called
+ * on every weight after each optimizer step, it is the per-step scale
+ * recalibration of section "Real-world performance gains".
+ *
+ *   w_bf16 : [N, K] bf16 payloads (input)
+ *   wq     : [N, K] E4M3 codes (output)
+ *   ws     : [N/128, K/128] fp32 scales (output); ws[nb, kb] covers rows
+ *            128*nb .. 128*nb+127, columns 128*kb .. 128*kb+127
+ *
+ * Same element rule as quant_act_1x128, with amax over the 16384 values of a
+ * block.  Errors: as quant_act_1x128, and UNSUPPORTED_SHAPE if N % 128 != 0.
+ */
+FP8BS_API int quant_w_128x128(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, int scale_mode,
+                    void *stream);
+
+/*
+ * quant_w_128x128_batched -- the weight quantizer over `count` independent
+ * tensors in one launch (the recalibration of every weight of a model after
+ * a step).  w_bf16[i], wq[i], ws[i], N[i], K[i] describe tensor i exactly as
+ * in quant_w_128x128.  The five arrays are HOST arrays of `count` entries,
+ * read during the call only; the pointers they hold are device pointers.
+ * Errors: as quant_w_128x128 for any tensor; INVALID_ARG if count < 0 or an
+ * array is null with count > 0.  count == 0 is a no-op.
+ */
+FP8BS_API int quant_w_128x128_batched(int64_t count, const void *const *w_bf16, const int64_t *N,
+                            const int64_t *K, void *const *wq, float *const *ws, int scale_mode,
+                            void *stream);
+
+/*
+ * fp8_block_gemm -- Y = dequant(Xq) * dequant(Wq)^T, the FP8 linear layer
+ * (article section "Technical breakthrough": linear layers run FP8 math).
+ *
+ *   xq [M, K] E4M3, xs [M, K/128] fp32     (from quant_act_1x128)
+ *   wq [N, K] E4M3, ws [N/128, K/128] fp32 (from quant_w_128x128)
+ *   y  [M, N] bf16 payloads or fp32 (out_dtype)
+ *
+ *   Y[m, n] = sum_kb (xs[m, kb] * ws[n/128, kb]) * P[m, n, kb],
+ *   P[m, n, kb] = sum_{k in block kb} decode(xq[m, k]) * decode(wq[n, k]),
+ * where P comes from FP8 matrix-core products accumulated in fp32 and the
+ * scale product is formed and applied in fp32 per 128-wide K block.  The
+ * order of the fp32 additions is the hardware's, so results agree with an
+ * exact evaluation to within fp32 rounding, not bit for bit; the bf16 output
+ * is the round-to-nearest-even of exactly the value the fp32 output holds.
+ * A given (M, N, K) always runs the same kernel: results are deterministic.
+ *
+ *   workspace, workspace_bytes: device scratch for split-K partial sums of
+ *   small-M shapes; fp8bs_gemm_workspace_size(M, N, K) gives the size needed
+ *   (0 for most shapes, where workspace may be NULL).  It need not be zeroed.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE (N or K not a multiple of 128),
+ * WORKSPACE_TOO_SMALL, UNSUPPORTED_DEVICE, HIP_ERROR.
+ */
+FP8BS_API int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                   int64_t K, void *y, int out_dtype, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/*
+ * fp8_block_grouped_gemm -- the MoE (mixture-of-experts) form of
+ * fp8_block_gemm (article section "Real-world performance gains": the recipe
+ * on Qwen3-30B, a mixture-of-experts model).
+ *
+ *   xq [M_total, K], xs [M_total, K/128]: token rows grouped by expert
+ *   wq [E, N, K], ws [E, N/128, K/128]: one weight matrix per expert
+ *   group_offsets: DEVICE int32 [E + 1]; rows group_offsets[e] ..
+ *     group_offsets[e+1]-1 belong to expert e.  The caller guarantees
+ *     group_offsets[0] == 0, non-decreasing, group_offsets[E] == M_total.
+ *     The host never reads them.  Empty groups are legal.  Offsets outside
+ *     [0, M_total] are clamped by the kernel, so they cannot cause an
+ *     out-of-bounds access (the result is then unspecified).
+ *   y [M_total, N]: row r holds fp8_block_gemm of row r with its expert.
+ * Workspace: fp8bs_grouped_workspace_size(E, M_total, N, K) bytes (0 today).
+ * Errors: as fp8_block_gemm; INVALID_ARG if E <= 0 with M_total > 0.
+ */
+FP8BS_API int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                           const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                           void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace sizes in bytes for the two GEMMs (pure functions of the shape; no device call). */
+FP8BS_API size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+FP8BS_API size_t fp8bs_grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+FP8BS_API const char *fp8bs_status_string(int status);
+
+/* FP8BS_ABI_VERSION of the built library. */
+FP8BS_API int fp8bs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -126,13 +126,13 @@ BF16_MAX_FINITE_BITS = 0x7F7F
 def pair_blocks(amax_lo: int, amax_hi: int, sign: int = 0) -> np.ndarray:
     """bf16 payloads [nblocks, 128] for every amax payload in [amax_lo, amax_hi)
     and every x payload in [0, amax]."""
-    a = np.arange(int(amax_lo), int(amax_hi), dtype=np.int64)
+    a = np.arange(int(amax_lo), int(amax_hi), dtype=np.int32)
     nx = a + 1
     nblk = (nx + 126) // 127
     blk_a = np.repeat(a, nblk)
-    first = np.repeat(np.cumsum(nblk) - nblk, nblk)
-    j = np.arange(blk_a.size, dtype=np.int64) - first
-    x = (j * 127)[:, None] + np.arange(127, dtype=np.int64)[None, :]
+    first = np.repeat(np.cumsum(nblk) - nblk, nblk).astype(np.int32)
+    j = np.arange(blk_a.size, dtype=np.int32) - first
+    x = (j * 127)[:, None] + np.arange(127, dtype=np.int32)[None, :]
     x[x > blk_a[:, None]] = 0
     out = np.empty((blk_a.size, 128), dtype=np.uint16)
     out[:, 0] = blk_a
@@ -142,7 +142,7 @@ def pair_blocks(amax_lo: int, amax_hi: int, sign: int = 0) -> np.ndarray:
     return out
 
 
-def pair_block_ranges(max_elems: int = 1 << 27):
+def pair_block_ranges(max_elems: int = 1 << 26):
     """Split [1, BF16_MAX_FINITE_BITS] into amax ranges whose pair blocks hold
     at most about ``max_elems`` elements each."""
     ranges = []

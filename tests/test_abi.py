@@ -1,0 +1,129 @@
+"""The C-ABI library: it loads, exports every function include/fp8bs.h declares,
+and rejects bad arguments before touching a device.
+
+These run on any host: every call below fails validation (or is a pure query)
+before the library makes a HIP call, except the device-check test, which only
+asks the runtime which device is current and is skipped when a GPU is present.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+
+@pytest.fixture(scope="module")
+def fp8bs():
+    import block_scaled_fp8_x128_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from block_scaled_fp8_x128_amd import build
+        build.build()
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^FP8BS_API\s+(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for fn in ("quant_act_1x128", "quant_w_128x128", "fp8_block_gemm", "fp8_block_grouped_gemm"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(fp8bs):
+    L = fp8bs.lib()
+    names = _declared_functions()
+    assert set(names) == set(fp8bs.EXPORTS)
+    for fn in names:
+        assert hasattr(L, fn), fn
+    # and nothing else: internal C++ symbols stay hidden
+    out = os.popen("nm -D --defined-only %s" % fp8bs.LIB_PATH).read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(names)
+
+
+def test_version_and_status_strings(fp8bs):
+    assert fp8bs.abi_version() == 1
+    for st in range(6):
+        s = fp8bs.status_string(st)
+        assert isinstance(s, str) and len(s) > 1
+    assert fp8bs.status_string(99) == "unknown status"
+
+
+def test_workspace_queries_are_pure(fp8bs):
+    L = fp8bs.lib()
+    assert L.fp8bs_gemm_workspace_size(0, 128, 128) == 0
+    assert L.fp8bs_gemm_workspace_size(-1, 128, 128) == 0
+    assert L.fp8bs_grouped_workspace_size(128, 65536, 1536, 2048) == 0
+    for M in (1, 16, 64, 256, 8192):
+        assert L.fp8bs_gemm_workspace_size(M, 28672, 4096) >= 0
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+MISAL = ctypes.c_void_p(0x10008)     # 8-byte aligned only
+NULL = ctypes.c_void_p(0)
+
+
+def test_quant_act_validation(fp8bs):
+    L = fp8bs.lib()
+    q = L.quant_act_1x128
+    assert q(FAKE, 4, 100, FAKE, FAKE, 0, NULL) == 2      # K % 128
+    assert q(FAKE, -1, 128, FAKE, FAKE, 0, NULL) == 1     # negative M
+    assert q(FAKE, 4, 0, FAKE, FAKE, 0, NULL) == 1        # K == 0
+    assert q(FAKE, 4, 128, FAKE, FAKE, 7, NULL) == 1      # unknown mode
+    assert q(NULL, 4, 128, FAKE, FAKE, 0, NULL) == 1      # null input
+    assert q(FAKE, 4, 128, NULL, FAKE, 0, NULL) == 1      # null codes
+    assert q(FAKE, 4, 128, FAKE, NULL, 0, NULL) == 1      # null scales
+    assert q(MISAL, 4, 128, FAKE, FAKE, 0, NULL) == 1     # misaligned input
+    assert q(NULL, 0, 128, NULL, NULL, 0, NULL) == 0      # M == 0: no-op
+
+
+def test_quant_w_validation(fp8bs):
+    L = fp8bs.lib()
+    q = L.quant_w_128x128
+    assert q(FAKE, 100, 128, FAKE, FAKE, 0, NULL) == 2     # N % 128
+    assert q(FAKE, 128, 130, FAKE, FAKE, 0, NULL) == 2     # K % 128
+    assert q(FAKE, 128, 128, FAKE, FAKE, -1, NULL) == 1
+    assert q(NULL, 0, 128, NULL, NULL, 1, NULL) == 0
+    b = L.quant_w_128x128_batched
+    assert b(-1, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 1
+    assert b(0, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 0
+    assert b(2, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 1
+    arr = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    Ns = (ctypes.c_int64 * 2)(128, 100)
+    Ks = (ctypes.c_int64 * 2)(128, 128)
+    assert b(2, arr, Ns, Ks, arr, arr, 0, NULL) == 2      # second tensor N % 128
+
+
+def test_gemm_validation(fp8bs):
+    L = fp8bs.lib()
+    g = L.fp8_block_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 100, 128, FAKE, 0, NULL, 0, NULL) == 2   # N % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 100, FAKE, 0, NULL, 0, NULL) == 2   # K % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, -8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1  # M < 0
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, FAKE, 5, NULL, 0, NULL) == 1   # out dtype
+    assert g(FAKE, FAKE, NULL, FAKE, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1   # null weights
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, NULL, 0, NULL, 0, NULL) == 1   # null output
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, MISAL, 0, NULL, 0, NULL) == 1  # misaligned output
+    assert g(NULL, NULL, FAKE, FAKE, 0, 128, 128, NULL, 0, NULL, 0, NULL) == 0   # M == 0
+    gg = L.fp8_block_grouped_gemm
+    assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1   # E == 0
+    assert gg(FAKE, FAKE, FAKE, FAKE, NULL, 4, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1   # null offsets
+    assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 128, FAKE, 0, NULL, 0, NULL) == 2    # N % 128
+    assert gg(NULL, NULL, FAKE, FAKE, FAKE, 4, 0, 128, 128, NULL, 0, NULL, 0, NULL) == 0   # empty
+
+
+def test_unsupported_device_without_gpu(fp8bs):
+    """Valid arguments on a host with no HIP device: UNSUPPORTED_DEVICE, nothing launched."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    L = fp8bs.lib()
+    assert L.quant_act_1x128(FAKE, 4, 128, FAKE, FAKE, 0, NULL) == 3
+    assert L.fp8_block_gemm(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 3
