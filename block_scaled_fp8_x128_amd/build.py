@@ -25,6 +25,9 @@ ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the GEMMs rescale every product with VALU FMAs,
+    # which cannot read AGPRs (each would need a v_accvgpr_read first)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC,
 ]
 

@@ -34,6 +34,9 @@
 #include "fp8bs_device.hpp"
 #include "fp8bs_internal.hpp"
 
+#include <stdlib.h>
+#include <string.h>
+
 namespace fp8bs {
 
 constexpr int BK = 128;        // K block = scale block
@@ -295,15 +298,414 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
     }
 }
 
+// ---- large-tile kernels: direct global->LDS loads -------------------------------
+//
+// Same product as gemm_kernel, organized for the dense prefill/training
+// shapes (M in the thousands):
+//   - large workgroup tiles (BM x BN = 256 x 256 over 8 waves, or 128 x 256
+//     over 4) of 64 x 128 wave tiles, so each K block moves (BM + BN) * 128
+//     bytes for 2 * BM * BN * 128 FLOP and each wave reads 24 KiB of LDS per
+//     32 MFMAs.  With 8 waves each SIMD holds two, so one wave's fp32 rescale
+//     (VALU) runs while the other's MFMAs keep the matrix core busy;
+//   - operands and activation scales go from global memory straight into LDS
+//     (buffer_load ... lds: each dwordx4 wave instruction fills 1 KiB = 8 LDS
+//     rows of 128 bytes, lane i writing bytes 16i .. 16i+15), so no VGPRs or
+//     VALU cycles are spent on staging.  The per-lane offset is fixed for the
+//     whole loop and the K block advances through the scalar offset;
+//   - LDS layout.  A 16-lane group of a ds_read_b128 fragment read touches 16
+//     rows at one K chunk; gfx950 serves it without bank conflicts when each
+//     8-lane half stays within one 128-byte half of the 256-byte bank space
+//     and the 8 lanes of a half hit 8 different 16-byte slots.  So tile row r
+//     of each 16-row group lives at LDS row ((r & 7) << 1) | (r >> 3) (rows
+//     0-7 on even rows, 8-15 on odd rows) and its 16-byte chunk c at slot
+//     c ^ (r & 7).  The LDS position of a DMA lane is fixed by the hardware,
+//     so the layout is produced on the global side: the lane that fills LDS
+//     row p, slot s fetches the chunk s ^ (r & 7) of the tile row r stored
+//     there -- still 8 lanes per 128-byte row, fully coalesced;
+//   - STAGES LDS buffers: the loads of block kb + STAGES - 1 are in flight
+//     while block kb is multiplied; one barrier per K block both publishes
+//     block kb and retires the reads of the buffer the next loads refill.
+//     Waits are explicit (s_waitcnt vmcnt with the count of loads issued after
+//     the ones needed), with every count a compile-time constant;
+//   - the weight scale of a K block is one scalar load; each wave fetches the
+//     activation scales of its own 64 rows (one dword per lane) with its
+//     operands, into a region of the stage that only it reads.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES_>
+struct DmaCfg {
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NT = NW * 64;
+    static constexpr int WM = BM / WAVES_M;
+    static constexpr int WN = BN / WAVES_N;
+    static constexpr int TM = WM / 16;
+    static constexpr int TN = WN / 16;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int XS_OFF = (BM + BN) * BK;            // activation scales after the operand rows
+    static constexpr int STAGE_BYTES = XS_OFF + NW * 256;    // 64 fp32 per wave
+    static constexpr int XG = BM / 8 / NW; // 1 KiB row groups of X per wave per stage
+    static constexpr int WG = BN / 8 / NW; // ... of W
+    static constexpr int DPW = XG + WG + 1; // LDS-DMA instructions per wave per stage (+1: scales)
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "row groups must split evenly over the waves");
+    static_assert(BM % 16 == 0, "16-row layout groups must not straddle X and W");
+    static_assert(WM == 64, "one activation-scale dword per lane covers the wave's 64 rows");
+    static_assert(WN % 16 == 0, "wave tile must be made of 16x16 MFMA tiles");
+    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-wide weight scale block");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+};
+
+// LDS row of tile row r, and the tile row held by LDS row p (inverse maps).
+__device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int tile_row(int p) { return (p & ~15) | ((p & 1) << 3) | ((p >> 1) & 7); }
+
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left alone (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3:
+// 32-bit data format, no swizzle); loads past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes >= 0xffffffffLL ? (int)0xffffffffu : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+// Geometry of one output tile of the persistent kernels.
+struct TileGeo {
+    int64_t row_begin, row_end; // rows of X / Y: [row_begin, row_end)
+    int64_t n0;                 // first column of Y (row of W)
+    const uint8_t *wq;          // this tile's weight matrix (the expert's, for the grouped form)
+    const float *ws;
+};
+
+// Tile of virtual id v (< tiles_m * tiles_n), or false for a grouped tile
+// past the last row tile of its expert list.
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int ntiles, TileGeo &g)
+{
+    int tm, tn;
+    tile_of(v, ntiles, a.tiles_m, a.tiles_n, tm, tn);
+    g.wq = a.wq;
+    g.ws = a.ws;
+    if (GROUPED) {
+        int e;
+        if (!expert_of_tile<BM>(a.offsets, a.E, a.M, tm, e, g.row_begin, g.row_end))
+            return false;
+        g.wq += (int64_t)e * a.N * a.K;
+        g.ws += (int64_t)e * (a.N / 128) * (a.K / BK);
+    } else {
+        g.row_begin = (int64_t)tm * BM;
+        g.row_end = (g.row_begin + BM) < a.M ? (g.row_begin + BM) : a.M;
+    }
+    g.n0 = (int64_t)tn * BN;
+    return true;
+}
+
+// Persistent form: gridDim.x workgroups (one per CU) walk the virtual tiles
+// v = blockIdx.x, blockIdx.x + gridDim.x, ...  All (tile, K block) steps of
+// a workgroup form one stream through the two LDS stages, so the first
+// blocks of the next tile are loaded while the current one finishes, and its
+// output stores drain while the next tile computes.  Stores are buffer
+// stores whose out-of-range rows the hardware drops, so every wave issues
+// exactly TM * TN of them per tile and the wait at the top of a step is an
+// exact count: "at most (stores issued after this step's loads) younger
+// memory operations outstanding" (vector memory operations complete in
+// issue order).
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs a)
+{
+    using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>;
+    constexpr int NST = C::TM * C::TN; // stores per wave per tile
+    static_assert(NST < 64, "the store count must fit the vmcnt field");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::STAGES * C::STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+    const int64_t K = a.K, KB = K / BK, N = a.N;
+    const int ntiles = a.tiles_m * a.tiles_n;
+    const int sub = lane >> 3, slot = lane & 7;
+    const int fr = lane & 15, fg = lane >> 4;
+
+    // ---- DMA cursor: the tile and K block whose operands load next ----
+    int dv = blockIdx.x;
+    TileGeo dt;
+    bool dvalid = false;
+    while (dv < ntiles && !(dvalid = tile_geo<BM, BN, GROUPED>(a, dv, ntiles, dt)))
+        dv += gridDim.x;
+    if (!dvalid)
+        return; // no tile for this workgroup (uniform)
+    TileGeo ct = dt; // compute cursor's tile
+    int cv = dv;
+    int64_t dkb = 0;
+
+    // per-tile DMA state (resources in SGPRs, row offsets in VGPRs)
+    __amdgpu_buffer_rsrc_t xr, wr, sr;
+    uint32_t xoffs[C::XG], woffs[C::WG], soff;
+#pragma unroll
+    for (int t = 0; t < C::WG; ++t) {
+        const int r = tile_row((wave + C::NW * t) * 8 + sub); // W row within the tile
+        woffs[t] = (uint32_t)(r * K) + (uint32_t)((slot ^ (r & 7)) << 4);
+    }
+    // Resources start at the tile's first X / W row and span the rows it may
+    // read; per-lane offsets are 32-bit (the launcher only picks this kernel
+    // when max(BM, BN) * K < 2^32).  Rows past the end of the tile's rows
+    // re-read the last one (never stored).
+    auto dma_setup = [&](const TileGeo &g) {
+        const int64_t last = g.row_end - g.row_begin - 1;
+        xr = make_rsrc(a.xq + g.row_begin * K, (last + 1) * K);
+        wr = make_rsrc(g.wq + g.n0 * K, (int64_t)BN * K);
+        sr = make_rsrc(a.xs + g.row_begin * KB, (last + 1) * KB * 4);
+#pragma unroll
+        for (int t = 0; t < C::XG; ++t) {
+            const int r = tile_row((wave + C::NW * t) * 8 + sub); // X row within the tile
+            const int64_t rr = r < last ? r : last;
+            xoffs[t] = (uint32_t)(rr * K) + (uint32_t)((slot ^ (r & 7)) << 4);
+        }
+        const int64_t rr = (wm * C::WM + lane) < last ? (wm * C::WM + lane) : last;
+        soff = (uint32_t)(rr * KB * 4);
+    };
+    auto issue = [&](int64_t kb, int stage) {
+        uint8_t *L = lds + stage * C::STAGE_BYTES;
+        const int ko = (int)(kb * BK);
+#pragma unroll
+        for (int t = 0; t < C::XG; ++t)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (LDS_AS void *)(L + (wave + C::NW * t) * 1024), 16,
+                                                     (int)xoffs[t], ko, 0, 0);
+#pragma unroll
+        for (int t = 0; t < C::WG; ++t)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (LDS_AS void *)(L + BM * BK + (wave + C::NW * t) * 1024),
+                                                     16, (int)woffs[t], ko, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (LDS_AS void *)(L + C::XS_OFF + wave * 256), 4, (int)soff,
+                                                 (int)(kb * 4), 0, 0);
+    };
+    // advance the DMA cursor by one K block; false at the end of the stream
+    auto dma_next = [&]() {
+        if (++dkb < KB)
+            return true;
+        dkb = 0;
+        do {
+            dv += gridDim.x;
+        } while (dv < ntiles && !tile_geo<BM, BN, GROUPED>(a, dv, ntiles, dt));
+        if (dv >= ntiles)
+            return false;
+        dma_setup(dt);
+        return true;
+    };
+
+    // ---- fragment offsets within a stage ----
+    // Lane l reads tile row (l % 16) of a 16-row MFMA tile, K chunks 2 (l/16)
+    // and 2 (l/16) + 1; consecutive MFMA tiles are 2048 bytes apart, so one
+    // base per operand half plus immediates covers every fragment.
+    int xo[2], wo[2];
+    {
+        const int px = (wm * C::WM + lds_row(fr)) * BK, pw = (BM + wn * C::WN + lds_row(fr)) * BK;
+        xo[0] = px + (((2 * fg) ^ (fr & 7)) << 4);
+        xo[1] = px + (((2 * fg + 1) ^ (fr & 7)) << 4);
+        wo[0] = pw + (((2 * fg) ^ (fr & 7)) << 4);
+        wo[1] = pw + (((2 * fg + 1) ^ (fr & 7)) << 4);
+    }
+    const int so = C::XS_OFF + wave * 256 + fr * 4;
+
+    v4f acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto frag = [](const uint8_t *p0, const uint8_t *p1) {
+        const u32x4 lo = *(const u32x4 *)p0;
+        const u32x4 hi = *(const u32x4 *)p1;
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    // One K block: scales, fragments, MFMAs with the fp32 rescale.  The
+    // rescale of MFMA tile t is issued after the MFMA of tile t + 1, so the
+    // matrix core always has the next product queued while the VALU applies
+    // the previous one.
+    auto compute = [&](int64_t kb, int stage, const CONST_AS float *ws_row) {
+        const uint8_t *L = lds + stage * C::STAGE_BYTES;
+        const float sw = ws_row[kb];
+        float sc[C::TM];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            sc[i] = *(const float *)(L + so + i * 64) * sw;
+        v8i bx[C::TM];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            bx[i] = frag(L + xo[0] + i * 2048, L + xo[1] + i * 2048);
+        v8i aw = frag(L + wo[0], L + wo[1]);
+        v4f part[2];
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            v8i aw_next;
+            if (j + 1 < C::TN)
+                aw_next = frag(L + wo[0] + (j + 1) * 2048, L + wo[1] + (j + 1) * 2048);
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) {
+                const int t = j * C::TM + i;
+                part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                               0, 0, 0, 127, 0, 127);
+                if (t > 0) {
+                    const int pi = (t - 1) % C::TM, pj = (t - 1) / C::TM;
+                    acc[pi][pj] = __builtin_elementwise_fma(v4f{sc[pi], sc[pi], sc[pi], sc[pi]}, part[(t - 1) & 1],
+                                                            acc[pi][pj]);
+                }
+            }
+            if (j + 1 < C::TN)
+                aw = aw_next;
+            // issue order of this group: the first MFMA, the next group's
+            // fragment reads (a whole group of MFMAs to land), then each
+            // remaining MFMA followed by the previous tile's rescale
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (j + 1 < C::TN)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+            for (int i = 1; i < C::TM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
+        constexpr int T = C::TM * C::TN;
+        acc[C::TM - 1][C::TN - 1] = __builtin_elementwise_fma(
+            v4f{sc[C::TM - 1], sc[C::TM - 1], sc[C::TM - 1], sc[C::TM - 1]}, part[(T - 1) & 1],
+            acc[C::TM - 1][C::TN - 1]);
+    };
+
+    // Output of a finished tile: buffer stores over the tile's own rows, so
+    // rows past row_end are dropped by the range check, not by a branch.
+    auto epilogue = [&](const TileGeo &g) {
+        constexpr int ES = OUT_F32 ? 4 : 2;
+        const __amdgpu_buffer_rsrc_t yr =
+            make_rsrc((const uint8_t *)a.y + (g.row_begin * N + g.n0) * ES, (g.row_end - g.row_begin) * N * ES);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+            const int m = wm * C::WM + i * 16 + fr;
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                const int n = wn * C::WN + j * 16 + fg * 4;
+                const int off = (int)(((int64_t)m * N + n) * ES);
+                const v4f v = acc[i][j];
+                if (OUT_F32) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yr, off, 0, 0);
+                } else {
+                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                    const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
+                    const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)}, yr, off, 0, 0);
+                }
+                acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    auto sync = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    dma_setup(dt);
+    issue(0, 0);
+    bool dmore = dma_next();
+    int stage = 0;
+    int64_t ckb = 0;
+    bool stores_after = false; // the previous step ended a tile: its stores follow this step's loads
+    const CONST_AS float *ws_row = (const CONST_AS float *)(ct.ws + ((ct.n0 + wn * C::WN) / 128) * KB);
+    while (true) {
+        if (stores_after)
+            wait_vmcnt<NST>(); // this step's operands landed; the stores may still drain
+        else
+            wait_vmcnt<0>();
+        sync(); // ... for every wave, and every wave is done reading the other stage
+        stores_after = false;
+        if (dmore) {
+            issue(dkb, stage ^ 1);
+            dmore = dma_next();
+        }
+        compute(ckb, stage, ws_row);
+        stage ^= 1;
+        if (++ckb == KB) {
+            epilogue(ct);
+            stores_after = true;
+            ckb = 0;
+            bool cvalid = false;
+            do {
+                cv += gridDim.x;
+            } while (cv < ntiles && !(cvalid = tile_geo<BM, BN, GROUPED>(a, cv, ntiles, ct)));
+            if (!cvalid)
+                break;
+            ws_row = (const CONST_AS float *)(ct.ws + ((ct.n0 + wn * C::WN) / 128) * KB);
+        }
+    }
+}
+
 // ---- variant table -----------------------------------------------------------------
+//
+// A shape picks its kernel from (M, N, K) alone -- never from out_dtype -- so
+// the fp32 and bf16 outputs of one shape come from the same arithmetic.
+// FP8BS_GEMM_VARIANT=simple|dma (read once) forces a kernel where its shape
+// constraints allow, for measurements.
+
+enum Variant { V_AUTO = 0, V_SIMPLE = 1, V_DMA = 2, V_DMA8 = 3 };
+
+static int forced_variant()
+{
+    static const int v = [] {
+        const char *e = getenv("FP8BS_GEMM_VARIANT");
+        if (!e)
+            return (int)V_AUTO;
+        if (!strcmp(e, "simple"))
+            return (int)V_SIMPLE;
+        if (!strcmp(e, "dma"))
+            return (int)V_DMA;
+        if (!strcmp(e, "dma8"))
+            return (int)V_DMA8;
+        return (int)V_AUTO;
+    }();
+    return v;
+}
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED>
-static hipError_t run(GemmArgs a, int grid, bool out_f32, hipStream_t stream)
+static hipError_t run_simple(GemmArgs a, int grid, bool out_f32, hipStream_t stream)
 {
     const dim3 block(WAVES_M * WAVES_N * 64);
     if (out_f32)
         return launch(gemm_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED>, dim3(grid), block, 0, stream, a);
     return launch(gemm_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED>, dim3(grid), block, 0, stream, a);
+}
+
+// Persistent launch: one workgroup per CU (at most one tile per workgroup
+// when there are fewer tiles than CUs); the count is a multiple of the 8
+// XCDs so that tile_of's XCD-contiguous ranges line up with the dispatch.
+constexpr int kPersistentGrid = 256;
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED>
+static hipError_t run_dma(GemmArgs a, int ntiles, bool out_f32, hipStream_t stream)
+{
+    const dim3 block(WAVES_M * WAVES_N * 64);
+    const int grid = ntiles < kPersistentGrid ? ntiles : kPersistentGrid;
+    if (out_f32)
+        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED>, dim3(grid), block, 0, stream, a);
+    return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED>, dim3(grid), block, 0, stream, a);
+}
+
+// The large-tile kernels: N a multiple of their 256-wide tile, 32-bit
+// LDS-DMA offsets (256 rows of K bytes) and 32-bit store offsets (256 rows of
+// N fp32), and enough rows for 128-row tiles to be worth it.
+static bool dma_ok(int64_t rows, int64_t N, int64_t K)
+{
+    return N % 256 == 0 && 256 * K < ((int64_t)1 << 32) && 256 * N * 4 < ((int64_t)1 << 31) && rows >= 128;
 }
 
 size_t gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
@@ -313,7 +715,6 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
 {
     if (M == 0)
         return hipSuccess;
-    constexpr int BM = 128, BN = 128;
     GemmArgs a = {};
     a.xq = (const uint8_t *)xq;
     a.xs = xs;
@@ -323,9 +724,20 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     a.M = M;
     a.N = N;
     a.K = K;
-    a.tiles_m = (int)((M + BM - 1) / BM);
-    a.tiles_n = (int)(N / BN);
-    return run<BM, BN, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    const int fv = forced_variant();
+    if (fv != V_SIMPLE && fv != V_DMA && dma_ok(M, N, K) && M >= 256) {
+        a.tiles_m = (int)((M + 255) / 256);
+        a.tiles_n = (int)(N / 256);
+        return run_dma<256, 256, 4, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    }
+    if (fv != V_SIMPLE && dma_ok(M, N, K)) {
+        a.tiles_m = (int)((M + 127) / 128);
+        a.tiles_n = (int)(N / 256);
+        return run_dma<128, 256, 2, 4, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    }
+    a.tiles_m = (int)((M + 127) / 128);
+    a.tiles_n = (int)(N / 128);
+    return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
@@ -334,7 +746,6 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
 {
     if (M_total == 0)
         return hipSuccess;
-    constexpr int BM = 128, BN = 128;
     GemmArgs a = {};
     a.xq = (const uint8_t *)xq;
     a.xs = xs;
@@ -346,9 +757,14 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
     a.N = N;
     a.K = K;
     a.E = E;
-    a.tiles_m = (int)((M_total + BM - 1) / BM + E);
-    a.tiles_n = (int)(N / BN);
-    return run<BM, BN, 2, 2, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    a.tiles_m = (int)((M_total + 127) / 128 + E);
+    const int fv = forced_variant();
+    if (fv != V_SIMPLE && dma_ok(M_total, N, K)) {
+        a.tiles_n = (int)(N / 256);
+        return run_dma<128, 256, 2, 4, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    }
+    a.tiles_n = (int)(N / 128);
+    return run_simple<128, 128, 2, 2, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
 }
 
 } // namespace fp8bs
