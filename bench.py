@@ -1,6 +1,6 @@
 """Benchmark of the block-FP8 linear-layer hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input.
+One step = one pass of the whole hot path over one batch of synthetic input.
 Workloads (--workload):
   dense  (default) 8B-shaped dense layer at M = 8192 tokens: per-step
          recalibration of the layer's four weights (128x128 quantizer), the
@@ -14,48 +14,71 @@ Workloads (--workload):
          routed top-8: expert-weight recalibration, quantization of the
          gate+up and down inputs, the two grouped GEMMs.
 Prints ONE JSON line.  `value` is GEMM TFLOP/s over the whole step
-(quantizers included) except for `recal` (GB/s); per-kernel times come from
-HIP events on the stream the kernels run on.
+(quantizers included) except for `recal` (GB/s).  Per-kernel times come from
+HIP events recorded on the stream the library launches on (torch's current
+stream, whose handle every call passes to the library).
+
+Tool modes (no GPU work of their own):
+  --copy-calibration   after the timed steps, copy a 1 GiB buffer three times
+                       (a plain copy kernel of known size, the reference for
+                       scaling rocprofv3 FETCH_SIZE / WRITE_SIZE);
+  --summarize-pmc FETCH_DB WRITE_DB  turn two rocprofv3 --pmc databases of
+                       `bench.py --copy-calibration` into the traffic record
+                       profiles/<kernel>_traffic.json that the roofline reads.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
 
 import numpy as np
-import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-
-import synth  # noqa: E402
 
 METRIC = "block-FP8 GEMM TFLOP/s (% of FP8 MFMA peak); quantizer GB/s (% of HBM peak)"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
 
 DENSE = [("qkv", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336), ("o_proj", 4096, 4096)]
+GEMM_SRC = os.path.join(ROOT, "block_scaled_fp8_x128_amd", "csrc", "fp8bs_gemm.hip")
+QUANT_SRC = os.path.join(ROOT, "block_scaled_fp8_x128_amd", "csrc", "fp8bs_quant.hip")
+COPY_BYTES = 1 << 30
+
+# Dominant kernel of each workload: (kernel-name prefix in a rocprofv3 trace,
+# source file, traffic record under profiles/).
+DOMINANT = {
+    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false>", GEMM_SRC,
+              "gemm_dma_256x256_dense_m8192_traffic.json"),
+    "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def bf16_dev(bits: np.ndarray, dev) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
 
 class KernelTimer:
-    """Per-kernel HIP-event timing on torch's current stream (the library's stream)."""
+    """Per-call HIP-event timing on torch's current stream (the library's stream)."""
 
     def __init__(self):
         self.pairs = {}
 
     def run(self, name, fn):
+        import torch
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -73,6 +96,7 @@ class KernelTimer:
 
 
 def timed_loop(step, steps, warmup, timer):
+    import torch
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
@@ -88,11 +112,43 @@ def maybe(timer, name, fn):
     return timer.run(name, fn) if timer is not None else fn()
 
 
+def bf16_dev(bits: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def hbm_entry(ms, nbytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def mfma_entry(ms, flops):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+
+
+def traffic_for(workload):
+    """HBM bytes per launch of the dominant kernel from its committed
+    rocprofv3 record, or None if there is none or the kernel source changed."""
+    if workload not in DOMINANT:
+        return None, None
+    _, src, fname = DOMINANT[workload]
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
+        return None, None
+    rec = json.load(open(path))
+    if rec.get("source_sha256_16") != src_hash(src):
+        return None, "stale: %s was taken before the last change of %s" % (fname, os.path.basename(src))
+    return rec["hbm_bytes_per_launch"], "profiles/" + fname
+
+
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
 
 def dense_workload(fp8bs, dev, mode):
+    import synth
+    import torch
     M = 8192
     bufs = []
     for i, (name, N, K) in enumerate(DENSE):
@@ -118,25 +174,30 @@ def dense_workload(fp8bs, dev, mode):
     return step, bufs, flops
 
 
-def summarize_dense(bufs, timer, ms_step, flops):
+def summarize_dense(bufs, timer):
     kernels = {}
+    gemm_ms, gemm_flops = [], []
     for b in bufs:
         M, N, K = b["M"], b["N"], b["K"]
         t = timer.avg_ms("gemm_" + b["name"])
-        tf = 2.0 * M * N * K / (t * 1e-3) / 1e12
-        kernels["gemm_" + b["name"]] = {"ms": round(t, 4), "TFLOP/s": round(tf, 1),
-                                        "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
-        for q, R, C in (("quant_act_", M, K), ("quant_w_", N, K)):
-            tq = timer.avg_ms(q + b["name"])
-            nbytes = R * C * 3 + (R * C // (128 if q == "quant_act_" else 16384)) * 4
-            gbs = nbytes / (tq * 1e-3) / 1e9
-            kernels[q + b["name"]] = {"ms": round(tq, 4), "GB/s": round(gbs, 1),
-                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    g = bufs[1]  # gate+up: the largest GEMM, most of the step's FLOPs
-    t = timer.avg_ms("gemm_gate_up")
-    ach = 2.0 * g["M"] * g["N"] * g["K"] / (t * 1e-3) / 1e12
-    roof = {"kernel": "gemm_kernel (gate+up, M8192 N28672 K4096)", "bound": "mfma", "achieved": round(ach, 1),
-            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None}
+        kernels["gemm_" + b["name"]] = mfma_entry(t, 2.0 * M * N * K)
+        gemm_ms.append(t)
+        gemm_flops.append(2.0 * M * N * K)
+        kernels["quant_act_" + b["name"]] = hbm_entry(timer.avg_ms("quant_act_" + b["name"]),
+                                                      M * K * 3 + (M * K // 128) * 4)
+        kernels["quant_w_" + b["name"]] = hbm_entry(timer.avg_ms("quant_w_" + b["name"]),
+                                                    N * K * 3 + (N * K // 16384) * 4)
+    # The four GEMMs run one kernel (the 256 x 256 persistent block-scaled
+    # GEMM): per launch, mean algorithmic FLOP / mean duration.
+    mean_ms = sum(gemm_ms) / len(gemm_ms)
+    mean_flops = sum(gemm_flops) / len(gemm_flops)
+    ach = mean_flops / (mean_ms * 1e-3) / 1e12
+    traffic, tsrc = traffic_for("dense")
+    roof = {"kernel": DOMINANT["dense"][0] + " (QKV, gate+up, down, o_proj at M=8192)", "bound": "mfma",
+            "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+            "algorithmic_flop_per_launch": mean_flops, "avg_launch_ms": round(mean_ms, 4),
+            "traffic_source": tsrc}
     return kernels, roof
 
 
@@ -144,6 +205,7 @@ def cpu_baseline_dense(target_s=12.0):
     """The oracle GEMM (exact per-block sums, fp64 scales) on a bounded sample
     of the gate+up GEMM: the first R rows of Y, R sized for ~target_s."""
     import oracle
+    import synth
     N, K = 28672, 4096
     threads = oracle.max_threads()
     w = synth.weights(N, K, sub=synth.sub_layer(1))
@@ -160,10 +222,12 @@ def cpu_baseline_dense(target_s=12.0):
         rows = min(8192, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 1.05)))
     tflops = 2.0 * rows * N * K / dt / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "gate+up GEMM, first %d of 8192 rows (N 28672, K 4096), %.1f s" % (rows, dt)}
+            "sample": "gate+up GEMM (N 28672, K 4096), first %d of 8192 rows, %.1f s wall" % (rows, dt)}
 
 
 def recal_workload(fp8bs, dev):
+    import synth
+    import torch
     shapes = [(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)]
     log("generating 32 layers x 4 bf16 weights on the device (seeded torch generator)")
     ws_in, outs = [], []
@@ -185,20 +249,178 @@ def recal_workload(fp8bs, dev):
     return step, nbytes
 
 
+def cpu_baseline_recal(target_s=12.0):
+    """The oracle's 128x128 quantizer on a bounded sample of the recalibration:
+    whole 28672 x 4096 weight tensors until ~target_s."""
+    import oracle
+    import synth
+    w = synth.weights(28672, 4096, sub=synth.sub_layer(0))
+    n, t = 0, 0.0
+    while t < target_s and n < 16:
+        t0 = time.perf_counter()
+        oracle.quant_w_128x128(w, 0)
+        t += time.perf_counter() - t0
+        n += 1
+    nbytes = n * (w.size * 3 + (w.size // 16384) * 4)
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "%d quantizations (EXACT) of one 28672 x 4096 weight, %.1f s wall" % (n, t)}
+
+
+def decode_workload(fp8bs, dev, mode):
+    import synth
+    import torch
+    pairs = []
+    for wname, N, K in (("gate_up", 28672, 4096), ("down", 4096, 14336)):
+        log("generating %s weights [%d, %d]" % (wname, N, K))
+        # five weight copies rotated over the steps, so that the 256 MB
+        # infinity cache never holds the weights a GEMM reads
+        copies = []
+        for c in range(5):
+            wq, ws = fp8bs.quant_w_128x128(bf16_dev(synth.weights(N, K, sub=synth.sub_layer(40 + c)), dev), mode)
+            copies.append((wq, ws))
+        for M in (1, 16, 64, 256):
+            x = bf16_dev(synth.activations(M, K, sub=synth.SUB_X + M), dev)
+            pairs.append(dict(name="%s_m%d" % (wname, M), M=M, N=N, K=K, x=x, copies=copies,
+                              xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                              xs=torch.empty((M, K // 128), dtype=torch.float32, device=dev),
+                              y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                              ws_buf=torch.empty(max(1, fp8bs.gemm_workspace_size(M, N, K)), dtype=torch.uint8,
+                                                 device=dev)))
+    it = [0]
+
+    def step(timer):
+        c = it[0] % 5
+        it[0] += 1
+        for p in pairs:
+            wq, ws = p["copies"][c]
+
+            def run(p=p, wq=wq, ws=ws):
+                fp8bs.quant_act_1x128(p["x"], mode, out=(p["xq"], p["xs"]))
+                fp8bs.fp8_block_gemm(p["xq"], p["xs"], wq, ws, out=p["y"], workspace=p["ws_buf"])
+            maybe(timer, "decode_" + p["name"], run)
+
+    flops = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pairs)
+    return step, pairs, flops
+
+
+def moe_workload(fp8bs, dev, mode):
+    import synth
+    import torch
+    E, H, F, T, TOPK = 128, 2048, 768, 8192, 8
+    row_token, offs = synth.moe_routing(T, E, TOPK)
+    Mt = int(offs[-1])
+    log("MoE: %d routed rows, per-expert rows min %d max %d" % (Mt, int(np.diff(offs).min()), int(np.diff(offs).max())))
+    x_tok = synth.activations(T, H, sub=synth.SUB_X)
+    x1 = bf16_dev(x_tok[row_token], dev)
+    x2 = bf16_dev(synth.activations(Mt, F, sub=synth.SUB_X + 1), dev)
+    w1 = bf16_dev(synth.expert_weights(E, 2 * F, H, sub=synth.SUB_W).reshape(E * 2 * F, H), dev)
+    w2 = bf16_dev(synth.expert_weights(E, H, F, sub=synth.SUB_W + 1).reshape(E * H, F), dev)
+    offs_d = torch.from_numpy(offs).to(dev)
+    b = dict(
+        x1q=torch.empty((Mt, H), dtype=torch.uint8, device=dev), x1s=torch.empty((Mt, H // 128), dtype=torch.float32,
+                                                                                  device=dev),
+        x2q=torch.empty((Mt, F), dtype=torch.uint8, device=dev), x2s=torch.empty((Mt, F // 128), dtype=torch.float32,
+                                                                                  device=dev),
+        w1q=torch.empty((E * 2 * F, H), dtype=torch.uint8, device=dev),
+        w1s=torch.empty((E * 2 * F // 128, H // 128), dtype=torch.float32, device=dev),
+        w2q=torch.empty((E * H, F), dtype=torch.uint8, device=dev),
+        w2s=torch.empty((E * H // 128, F // 128), dtype=torch.float32, device=dev),
+        y1=torch.empty((Mt, 2 * F), dtype=torch.bfloat16, device=dev),
+        y2=torch.empty((Mt, H), dtype=torch.bfloat16, device=dev))
+
+    def step(timer):
+        maybe(timer, "quant_w_experts", lambda: fp8bs.quant_w_128x128_batched([w1, w2], mode,
+                                                                               outs=[(b["w1q"], b["w1s"]),
+                                                                                     (b["w2q"], b["w2s"])]))
+        maybe(timer, "quant_act_gate_up", lambda: fp8bs.quant_act_1x128(x1, mode, out=(b["x1q"], b["x1s"])))
+        maybe(timer, "grouped_gate_up", lambda: fp8bs.fp8_block_grouped_gemm(
+            b["x1q"], b["x1s"], b["w1q"].view(E, 2 * F, H), b["w1s"].view(E, 2 * F // 128, H // 128), offs_d,
+            out=b["y1"]))
+        maybe(timer, "quant_act_down", lambda: fp8bs.quant_act_1x128(x2, mode, out=(b["x2q"], b["x2s"])))
+        maybe(timer, "grouped_down", lambda: fp8bs.fp8_block_grouped_gemm(
+            b["x2q"], b["x2s"], b["w2q"].view(E, H, F), b["w2s"].view(E, H // 128, F // 128), offs_d, out=b["y2"]))
+
+    shapes = {"gate_up": (Mt, 2 * F, H), "down": (Mt, H, F)}
+    flops = sum(2.0 * m * n * k for m, n, k in shapes.values())
+    return step, shapes, flops, E
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 counter records
+# ---------------------------------------------------------------------------
+
+def _pmc_means(db, counter):
+    """Mean per-dispatch value of `counter` for every kernel name in a rocprofv3 database."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    per = {}
+    for kname, val, did in c.execute("select kernel_name, value, dispatch_id from counters_collection "
+                                     "where counter_name = ?", (counter,)):
+        per.setdefault(kname, {}).setdefault(did, 0.0)
+        per[kname][did] += val
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def summarize_pmc(fetch_db, write_db, workload, command):
+    kprefix, src, fname = DOMINANT[workload]
+    fetch = _pmc_means(fetch_db, "FETCH_SIZE")
+    write = _pmc_means(write_db, "WRITE_SIZE")
+
+    def pick(d, pred):
+        hits = [(k, v) for k, v in d.items() if pred(k)]
+        if not hits:
+            raise SystemExit("no kernel matched in the counter database")
+        return hits[0][1]
+    # torch's device-to-device copy of one buffer is the runtime's blit kernel
+    is_copy = lambda k: "copybuffer" in k.lower()  # noqa: E731
+    is_dom = lambda k: k.startswith("void " + kprefix) or k.startswith(kprefix)  # noqa: E731
+    # the calibration copy moves COPY_BYTES in and COPY_BYTES out per launch
+    copy_f, _ = pick(fetch, is_copy)
+    copy_w, _ = pick(write, is_copy)
+    kf, nf = pick(fetch, is_dom)
+    kw, nw = pick(write, is_dom)
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    rec = {"kernel": kprefix, "workload": workload, "command": command,
+           "source": os.path.relpath(src, ROOT), "source_sha256_16": src_hash(src),
+           "fetch_kib_per_launch_raw": kf, "write_kib_per_launch_raw": kw, "launches": [nf, nw],
+           "copy_fetch_kib_raw": copy_f, "copy_write_kib_raw": copy_w,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_fetch_bytes_per_launch": kf * 1024.0 * f_scale,
+           "hbm_write_bytes_per_launch": kw * 1024.0 * w_scale}
+    rec["hbm_bytes_per_launch"] = rec["hbm_fetch_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    out = os.path.join(ROOT, "profiles", fname)
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "recal"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "recal", "decode", "moe"])
     ap.add_argument("--mode", type=int, default=0, help="scale mode: 0 EXACT, 1 POW2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    ap.add_argument("--pmc-command", default="", help="the profiled command, recorded with --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every kernel runs on one GPU's share at its real shape); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import torch
     import block_scaled_fp8_x128_amd as fp8bs
     if not os.path.exists(fp8bs.LIB_PATH):
         from block_scaled_fp8_x128_amd import build
@@ -206,39 +428,93 @@ def main():
     fp8bs.lib()
     dev = torch.device("cuda", 0)
     timer = KernelTimer()
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
 
     if args.workload == "dense":
         step, bufs, flops = dense_workload(fp8bs, dev, args.mode)
         ms = timed_loop(step, args.steps, args.warmup, timer)
-        kernels, roof = summarize_dense(bufs, timer, ms, flops)
-        value = flops / (ms * 1e-3) / 1e12
-        out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-               "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-               "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        kernels, roof = summarize_dense(bufs, timer)
+        out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
+               "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "8B-shaped dense layer at M=8192 tokens: recalibrate 4 weights (128x128), "
                                       "quantize 4 inputs (1x128), GEMMs QKV K4096 N6144, gate+up K4096 N28672, "
                                       "down K14336 N4096, o_proj K4096 N4096",
                           "scale_mode": "pow2" if args.mode else "exact", "out_dtype": "bf16",
                           "gemm_flops_per_step": flops},
                "roofline": roof, "kernels": kernels}
-        if not args.no_cpu_baseline:
-            log("timing the oracle on the host (bounded sample)")
-            out["cpu_baseline"] = cpu_baseline_dense()
-    else:
+        cpu = (lambda: cpu_baseline_dense()) if not args.no_cpu_baseline else None
+    elif args.workload == "recal":
         step, nbytes = recal_workload(fp8bs, dev)
         ms = timed_loop(step, args.steps, args.warmup, timer)
         te, tp = timer.avg_ms("recal_exact"), timer.avg_ms("recal_pow2")
-        gbs = 2 * nbytes / (ms * 1e-3) / 1e9
-        out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-               "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-               "vs_baseline": None, "dtype": "bf16->fp8e4m3", "data": "synthetic",
+        traffic, tsrc = traffic_for("recal")
+        ach = nbytes / (te * 1e-3) / 1e9
+        out = {"metric": METRIC, "value": round(2 * nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", **common,
+               "ms_per_step": round(ms, 4), "dtype": "bf16->fp8e4m3",
                "config": {"workload": "per-step recalibration: 32 layers x {6144x4096, 4096x4096, 28672x4096, "
                                       "4096x14336} bf16 weights, 128x128 blocks, EXACT then POW2",
                           "bytes_per_pass": nbytes},
-               "roofline": {"kernel": "quant_w_kernel (batched)", "bound": "hbm",
-                            "achieved": round(nbytes / (te * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(nbytes / (te * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
-               "kernels": {"recal_exact": {"ms": round(te, 4)}, "recal_pow2": {"ms": round(tp, 4)}}}
+               "roofline": {"kernel": DOMINANT["recal"][0] + " (batched, EXACT)", "bound": "hbm",
+                            "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": tsrc},
+               "kernels": {"recal_exact": hbm_entry(te, nbytes), "recal_pow2": hbm_entry(tp, nbytes)}}
+        cpu = (lambda: cpu_baseline_recal()) if not args.no_cpu_baseline else None
+    elif args.workload == "decode":
+        step, pairs, flops = decode_workload(fp8bs, dev, args.mode)
+        ms = timed_loop(step, args.steps, args.warmup, timer)
+        kernels = {}
+        for p in pairs:
+            t = timer.avg_ms("decode_" + p["name"])
+            nbytes = p["N"] * p["K"] + p["N"] * p["K"] // 16384 * 4 + p["M"] * p["K"] * 3 + p["M"] * p["N"] * 2
+            kernels["decode_" + p["name"]] = {**hbm_entry(t, nbytes),
+                                              **{"TFLOP/s": round(2.0 * p["M"] * p["N"] * p["K"] / (t * 1e-3) / 1e12,
+                                                                  2)}}
+        big = max(pairs, key=lambda p: p["N"] * p["K"] + p["M"])
+        tb = timer.avg_ms("decode_" + big["name"])
+        nb = big["N"] * big["K"] * (1 + 4 / 16384) + big["M"] * big["K"] * 3 + big["M"] * big["N"] * 2
+        ach = nb / (tb * 1e-3) / 1e9
+        out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", **common,
+               "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
+               "config": {"workload": "rollout decode: M in {1,16,64,256} x (gate+up K4096 N28672, down K14336 "
+                                      "N4096), activations quantized on the fly, 5 rotated weight copies"},
+               "roofline": {"kernel": "quant_act_1x128 + fp8_block_gemm, %s" % big["name"], "bound": "hbm",
+                            "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None},
+               "kernels": kernels}
+        cpu = None
+    else:
+        step, shapes, flops, E = moe_workload(fp8bs, dev, args.mode)
+        ms = timed_loop(step, args.steps, args.warmup, timer)
+        kernels = {}
+        for name, (m, n, k) in shapes.items():
+            t = timer.avg_ms("grouped_" + name)
+            nbytes = m * k + m * k // 128 * 4 + E * n * k * (1 + 4 / 16384) + m * n * 2
+            kernels["grouped_" + name] = {**mfma_entry(t, 2.0 * m * n * k), **hbm_entry(t, nbytes)}
+            kernels["quant_act_" + name] = hbm_entry(timer.avg_ms("quant_act_" + name), m * k * 3 + m * k // 128 * 4)
+        t = timer.avg_ms("grouped_gate_up")
+        m, n, k = shapes["gate_up"]
+        ach = 2.0 * m * n * k / (t * 1e-3) / 1e12
+        out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
+               "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
+               "config": {"workload": "MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens top-8 "
+                                      "(65536 rows); grouped gate+up K2048 N1536 and down K768 N2048"},
+               "roofline": {"kernel": "fp8_block_grouped_gemm gate+up", "bound": "mfma", "achieved": round(ach, 1),
+                            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
+                            "traffic": None},
+               "kernels": kernels}
+        cpu = None
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).view(torch.bfloat16)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if cpu is not None:
+        log("timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"] = cpu()
     print(json.dumps(out), flush=True)
 
 
