@@ -369,6 +369,9 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) with vmcnt / expcnt left alone.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3:
 // 32-bit data format, no swizzle); loads past `bytes` return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
@@ -410,20 +413,17 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int ntiles, T
 
 // Persistent form: gridDim.x workgroups (one per CU) walk the virtual tiles
 // v = blockIdx.x, blockIdx.x + gridDim.x, ...  All (tile, K block) steps of
-// a workgroup form one stream through the two LDS stages, so the first
-// blocks of the next tile are loaded while the current one finishes, and its
-// output stores drain while the next tile computes.  Stores are buffer
-// stores whose out-of-range rows the hardware drops, so every wave issues
-// exactly TM * TN of them per tile and the wait at the top of a step is an
-// exact count: "at most (stores issued after this step's loads) younger
-// memory operations outstanding" (vector memory operations complete in
-// issue order).
+// a workgroup form one stream through the two LDS stages: the operands of
+// step s + 2 are issued in the middle of step s, as soon as every wave has
+// finished reading the stage they refill (a full step of lookahead), and the
+// fragments of step s + 1 are read into registers during the last MFMA
+// groups of step s, so the matrix cores never wait on LDS at a step
+// boundary; a tile's output stores drain while the next tile computes.  Stores are buffer stores
+// whose out-of-range rows the hardware drops.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs a)
 {
     using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>;
-    constexpr int NST = C::TM * C::TN; // stores per wave per tile
-    static_assert(NST < 64, "the store count must fit the vmcnt field");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::STAGES * C::STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -443,48 +443,56 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         dv += gridDim.x;
     if (!dvalid)
         return; // no tile for this workgroup (uniform)
-    TileGeo ct = dt; // compute cursor's tile
-    int cv = dv;
+    TileGeo ct = dt; // tile of the step being computed
     int64_t dkb = 0;
 
-    // per-tile DMA state (resources in SGPRs, row offsets in VGPRs)
-    __amdgpu_buffer_rsrc_t xr, wr, sr;
-    uint32_t xoffs[C::XG], woffs[C::WG], soff;
-#pragma unroll
-    for (int t = 0; t < C::WG; ++t) {
-        const int r = tile_row((wave + C::NW * t) * 8 + sub); // W row within the tile
-        woffs[t] = (uint32_t)(r * K) + (uint32_t)((slot ^ (r & 7)) << 4);
-    }
-    // Resources start at the tile's first X / W row and span the rows it may
-    // read; per-lane offsets are 32-bit (the launcher only picks this kernel
-    // when max(BM, BN) * K < 2^32).  Rows past the end of the tile's rows
-    // re-read the last one (never stored).
+    // ---- per-tile DMA state ----
+    // Row group t of a wave (LDS rows 8 (wave + NW t) .. + 7) holds tile rows
+    // tile_row(8 wave + sub) + 8 NW t: the same per-lane offset for every t,
+    // plus 8 NW t rows.  W adds those rows through the scalar offset.  X
+    // takes one buffer resource per row group, based at the group's first
+    // row and bounded by the tile's last row, so lanes past the end of a
+    // ragged tile read zeros through the hardware range check (those rows are
+    // never stored); the activation scales are bounded the same way.  Offsets
+    // are 32-bit (the launcher only picks this kernel when 256 K < 2^32).
+    constexpr int GROW = 8 * C::NW; // rows between a wave's consecutive row groups
+    // (the resources are rebuilt per issue from the tile's bases and row
+    // count: the host pass of this compiler emits no launch stub for a kernel
+    // holding an array of buffer resources)
+    const uint8_t *xbase, *wbase;
+    const float *sbase;
+    int64_t xrows;
+    const int r0 = tile_row(wave * 8 + sub);
+    const uint32_t loff = (uint32_t)(r0 * K) + (uint32_t)((slot ^ (r0 & 7)) << 4);
+    const uint32_t soff = (uint32_t)((wm * C::WM + lane) * KB * 4);
     auto dma_setup = [&](const TileGeo &g) {
-        const int64_t last = g.row_end - g.row_begin - 1;
-        xr = make_rsrc(a.xq + g.row_begin * K, (last + 1) * K);
-        wr = make_rsrc(g.wq + g.n0 * K, (int64_t)BN * K);
-        sr = make_rsrc(a.xs + g.row_begin * KB, (last + 1) * KB * 4);
-#pragma unroll
-        for (int t = 0; t < C::XG; ++t) {
-            const int r = tile_row((wave + C::NW * t) * 8 + sub); // X row within the tile
-            const int64_t rr = r < last ? r : last;
-            xoffs[t] = (uint32_t)(rr * K) + (uint32_t)((slot ^ (r & 7)) << 4);
-        }
-        const int64_t rr = (wm * C::WM + lane) < last ? (wm * C::WM + lane) : last;
-        soff = (uint32_t)(rr * KB * 4);
+        xbase = a.xq + g.row_begin * K;
+        xrows = g.row_end - g.row_begin;
+        wbase = g.wq + g.n0 * K;
+        sbase = a.xs + g.row_begin * KB;
     };
-    auto issue = [&](int64_t kb, int stage) {
+    // Loads of K block kb into `stage`.  With live == false every range is
+    // empty, so the same instructions move nothing (the hardware range check
+    // drops them): the caller issues them unconditionally, keeping the MFMA
+    // stream they sit in free of branches.
+    auto issue = [&](int64_t kb, int stage, bool live = true) {
         uint8_t *L = lds + stage * C::STAGE_BYTES;
         const int ko = (int)(kb * BK);
+        const int64_t rows = live ? xrows : 0;
 #pragma unroll
-        for (int t = 0; t < C::XG; ++t)
+        for (int t = 0; t < C::XG; ++t) {
+            const int64_t left = rows - (int64_t)GROW * t;
+            const __amdgpu_buffer_rsrc_t xr = make_rsrc(xbase + (int64_t)GROW * t * K, left > 0 ? left * K : 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (LDS_AS void *)(L + (wave + C::NW * t) * 1024), 16,
-                                                     (int)xoffs[t], ko, 0, 0);
+                                                     (int)loff, ko, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t wl = make_rsrc(wbase, live ? (int64_t)BN * K : 0);
 #pragma unroll
         for (int t = 0; t < C::WG; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (LDS_AS void *)(L + BM * BK + (wave + C::NW * t) * 1024),
-                                                     16, (int)woffs[t], ko, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (LDS_AS void *)(L + C::XS_OFF + wave * 256), 4, (int)soff,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wl, (LDS_AS void *)(L + BM * BK + (wave + C::NW * t) * 1024),
+                                                     16, (int)loff, ko + (int)(GROW * t * K), 0, 0);
+        const __amdgpu_buffer_rsrc_t sl = make_rsrc(sbase, rows * KB * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sl, (LDS_AS void *)(L + C::XS_OFF + wave * 256), 4, (int)soff,
                                                  (int)(kb * 4), 0, 0);
     };
     // advance the DMA cursor by one K block; false at the end of the stream
@@ -528,58 +536,101 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
 
-    // One K block: scales, fragments, MFMAs with the fp32 rescale.  The
-    // rescale of MFMA tile t is issued after the MFMA of tile t + 1, so the
-    // matrix core always has the next product queued while the VALU applies
-    // the previous one.
-    auto compute = [&](int64_t kb, int stage, const CONST_AS float *ws_row) {
+    // Fragments and scale products of the step being computed.  Except for
+    // the first step they are read from the step's LDS stage while the
+    // previous step's last two MFMA groups run.  W fragments rotate through
+    // a ring of three (the group being multiplied and the next two).
+    v8i bx[C::TM];
+    v8i awq[3];
+    float sc[C::TM];
+    auto ws_of = [&](const TileGeo &g) {
+        return (const CONST_AS float *)(g.ws + ((g.n0 + wn * C::WN) / 128) * KB);
+    };
+    auto sync = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto rescale = [&](int t, const v4f &p) {
+        const int i = t % C::TM, j = t / C::TM;
+        acc[i][j] = __builtin_elementwise_fma(v4f{sc[i], sc[i], sc[i], sc[i]}, p, acc[i][j]);
+    };
+    static_assert(C::TN >= 4, "the W-fragment ring needs at least four groups per step");
+
+    // One K block from registers.  Group j (TM MFMAs on one W fragment)
+    // reads the W fragment of group j + 2, so each LDS read has two groups of
+    // MFMAs to land.  The rescale of MFMA tile t is issued after the MFMA of
+    // tile t + 1, so the matrix core has the next product queued while the
+    // VALU applies the previous one.  Before group TN - 2 every wave waits for
+    // the next step's operands (the most recent loads it issued) and for its
+    // own LDS reads (the last read of this stage was issued in group TN - 3),
+    // and passes the barrier: the next stage is then complete for all waves
+    // and no wave reads this stage any more, so the loads issued at the top of
+    // the next step may refill it.  Groups TN - 2 and TN - 1 then read the
+    // next step's first two W fragments and scales, and each MFMA of the last
+    // group frees its X fragment registers for the next step's.  (For the last
+    // step of a workgroup those reads fetch data that is never used; the
+    // barrier is uniform.)
+    auto compute = [&](int stage, float sw_next, auto &&after_barrier) __attribute__((always_inline)) {
         const uint8_t *L = lds + stage * C::STAGE_BYTES;
-        const float sw = ws_row[kb];
-        float sc[C::TM];
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-            sc[i] = *(const float *)(L + so + i * 64) * sw;
-        v8i bx[C::TM];
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-            bx[i] = frag(L + xo[0] + i * 2048, L + xo[1] + i * 2048);
-        v8i aw = frag(L + wo[0], L + wo[1]);
+        const uint8_t *Ln = lds + (stage ^ 1) * C::STAGE_BYTES;
         v4f part[2];
+        float xs_next[C::TM];
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-            v8i aw_next;
-            if (j + 1 < C::TN)
-                aw_next = frag(L + wo[0] + (j + 1) * 2048, L + wo[1] + (j + 1) * 2048);
+            const bool last = j + 1 == C::TN;
+            if (j + 2 < C::TN) {
+                awq[(j + 2) % 3] = frag(L + wo[0] + (j + 2) * 2048, L + wo[1] + (j + 2) * 2048);
+            } else if (j + 2 == C::TN) {
+                wait_vmcnt<0>();
+                wait_lgkmcnt0();
+                sync();
+                after_barrier();
+                awq[(j + 2) % 3] = frag(Ln + wo[0], Ln + wo[1]);
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+                    xs_next[i] = *(const float *)(Ln + so + i * 64);
+            } else {
+                awq[(j + 2) % 3] = frag(Ln + wo[0] + 2048, Ln + wo[1] + 2048);
+            }
+            // the reads above stay ahead of this group's MFMAs (the machine
+            // scheduler would otherwise sink them to where the registers they
+            // fill are next used, shrinking the prefetch distance to zero)
+            __builtin_amdgcn_sched_barrier(0);
+            const v8i aw = awq[j % 3];
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 const int t = j * C::TM + i;
                 part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], v4f{0.f, 0.f, 0.f, 0.f},
                                                                                0, 0, 0, 127, 0, 127);
-                if (t > 0) {
-                    const int pi = (t - 1) % C::TM, pj = (t - 1) / C::TM;
-                    acc[pi][pj] = __builtin_elementwise_fma(v4f{sc[pi], sc[pi], sc[pi], sc[pi]}, part[(t - 1) & 1],
-                                                            acc[pi][pj]);
-                }
+                if (t > 0)
+                    rescale(t - 1, part[(t - 1) & 1]);
+                if (last)
+                    bx[i] = frag(Ln + xo[0] + i * 2048, Ln + xo[1] + i * 2048);
             }
-            if (j + 1 < C::TN)
-                aw = aw_next;
-            // issue order of this group: the first MFMA, the next group's
-            // fragment reads (a whole group of MFMAs to land), then each
-            // remaining MFMA followed by the previous tile's rescale
+            // issue order: each MFMA followed by the previous rescale (and in
+            // the last group by the next step's X fragment it freed)
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (j + 1 < C::TN)
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
 #pragma unroll
             for (int i = 1; i < C::TM; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (last)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
+            if (last)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        constexpr int T = C::TM * C::TN;
-        acc[C::TM - 1][C::TN - 1] = __builtin_elementwise_fma(
-            v4f{sc[C::TM - 1], sc[C::TM - 1], sc[C::TM - 1], sc[C::TM - 1]}, part[(T - 1) & 1],
-            acc[C::TM - 1][C::TN - 1]);
+        rescale(C::TM * C::TN - 1, part[(C::TM * C::TN - 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            sc[i] = xs_next[i] * sw_next;
+        // the next step's groups 0 and 1 were read into slots TN % 3 and
+        // (TN + 1) % 3; move them to slots 0 and 1
+        const v8i n0 = awq[C::TN % 3], n1 = awq[(C::TN + 1) % 3];
+        awq[0] = n0;
+        awq[1] = n1;
     };
 
     // Output of a finished tile: buffer stores over the tile's own rows, so
@@ -609,44 +660,77 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             }
         }
     };
-    auto sync = [&]() {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
 
+    // prologue: the first step's operands, fragments and scales
     dma_setup(dt);
     issue(0, 0);
     bool dmore = dma_next();
+    wait_vmcnt<0>();
+    sync();
+    {
+        const float sw = ws_of(ct)[0];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            sc[i] = *(const float *)(lds + so + i * 64) * sw;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            bx[i] = frag(lds + xo[0] + i * 2048, lds + xo[1] + i * 2048);
+        awq[0] = frag(lds + wo[0], lds + wo[1]);
+        awq[1] = frag(lds + wo[0] + 2048, lds + wo[1] + 2048);
+    }
+
+    // Lookahead: the operands of step s + 1 are in flight (or landed) while
+    // step s is computed; those of step s + 2 are issued right after the
+    // barrier in the middle of step s, the earliest point at which every wave
+    // has finished reading the stage they refill.  Per lookahead step only a
+    // flag and the address of its weight scale are carried; the tile of the
+    // step being computed advances with its own cursor.
+    int cv = dv;
+    bool has1 = dmore;
+    const CONST_AS float *wsp1 = ws_of(ct);
+    if (has1) {
+        wsp1 = ws_of(dt) + dkb;
+        issue(dkb, 1);
+        dmore = dma_next();
+    }
+
     int stage = 0;
     int64_t ckb = 0;
-    bool stores_after = false; // the previous step ended a tile: its stores follow this step's loads
-    const CONST_AS float *ws_row = (const CONST_AS float *)(ct.ws + ((ct.n0 + wn * C::WN) / 128) * KB);
+    bool advance = false; // the cursor's step was issued during the previous step
     while (true) {
-        if (stores_after)
-            wait_vmcnt<NST>(); // this step's operands landed; the stores may still drain
-        else
-            wait_vmcnt<0>();
-        sync(); // ... for every wave, and every wave is done reading the other stage
-        stores_after = false;
-        if (dmore) {
-            issue(dkb, stage ^ 1);
+        if (advance)
             dmore = dma_next();
+        float sw_next = 0.f;
+        if (has1) {
+            sw_next = *wsp1;
+            // Take the scalar load's result right away: loads through the
+            // scalar cache may return out of order, so while one is
+            // outstanding every wait for an LDS read has to be lgkmcnt(0),
+            // which would also wait for the fragment reads issued ahead.
+            asm volatile("" ::"s"(sw_next));
         }
-        compute(ckb, stage, ws_row);
+        const bool has2 = dmore;
+        const int64_t kb2 = dkb;
+        const CONST_AS float *wsp2 = has2 ? ws_of(dt) + dkb : wsp1;
+        // only the loads go in the middle of the MFMA stream; the cursor
+        // advances (and sets up the next tile's loads) at the top of the
+        // next step
+        compute(stage, sw_next, [&]() { issue(kb2, stage, has2); });
+        advance = has2;
         stage ^= 1;
         if (++ckb == KB) {
             epilogue(ct);
-            stores_after = true;
             ckb = 0;
-            bool cvalid = false;
-            do {
-                cv += gridDim.x;
-            } while (cv < ntiles && !(cvalid = tile_geo<BM, BN, GROUPED>(a, cv, ntiles, ct)));
-            if (!cvalid)
-                break;
-            ws_row = (const CONST_AS float *)(ct.ws + ((ct.n0 + wn * C::WN) / 128) * KB);
+            if (has1) {
+                do {
+                    cv += gridDim.x;
+                } while (!tile_geo<BM, BN, GROUPED>(a, cv, ntiles, ct));
+            }
         }
+        if (!has1)
+            break;
+        has1 = has2;
+        wsp1 = wsp2;
     }
 }
 
