@@ -734,6 +734,148 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     }
 }
 
+// ---- weight-streaming kernel for few activation rows (rollout decode) ------------
+//
+// With M <= 256 the product is bound by reading W from HBM.  A
+// workgroup owns TN * 16 rows of W and TM * 16 rows of X (blockIdx.y walks
+// the row chunks of X); its 8 waves split the K blocks (wave w takes blocks
+// w, w + 8, ...), so every W byte is loaded by exactly one wave, straight
+// from global memory into MFMA operand registers with D blocks in flight:
+// no LDS and no barrier in the main loop.  X rows past M read as zeros
+// through the buffer range check, and their scales as zeros.  At the end the
+// 8 per-wave partial tiles are summed through LDS in wave order (a fixed
+// order, so results are deterministic) and written out.
+template <int TM, int TN, int D, bool OUT_F32>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
+{
+    constexpr int NW = 8;
+    constexpr int LPB = 2 * TN + 3 * TM; // loads per K block: W lo/hi, X lo/hi, X scale
+    static_assert((D - 1) * LPB < 64, "outstanding loads must fit the vmcnt field");
+    __shared__ __attribute__((aligned(16))) float red[NW][TM * 16][TN * 16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int fr = lane & 15, fg = lane >> 4;
+    const int64_t K = a.K, KB = K / BK, N = a.N, M = a.M;
+    const int64_t n0 = (int64_t)blockIdx.x * (TN * 16);
+    const int64_t m0 = (int64_t)blockIdx.y * (TM * 16);
+    const int64_t mrows = (M - m0) < TM * 16 ? (M - m0) : TM * 16;
+
+    // W rows n0 .. n0 + 16 TN - 1 (all inside W: N % (16 TN) == 0); X rows
+    // m0 .. m0 + mrows - 1.  Lane offsets: row fr of a 16-row tile, bytes
+    // 32 fg .. 32 fg + 31 of the K block (the same K order for both operands).
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wq + n0 * K, (int64_t)TN * 16 * K);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.xq + m0 * K, mrows * K);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.xs + m0 * KB, mrows * KB * 4);
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(a.xq, 0);
+    const int loff = (int)(fr * K + fg * 32);
+    const int soff = (int)(fr * KB * 4);
+    const CONST_AS float *ws_row = (const CONST_AS float *)(a.ws + (n0 / 128) * KB);
+
+    const int nk = wave < KB ? (int)((KB - wave + NW - 1) / NW) : 0; // this wave's K blocks
+
+    v8i wf[D][TN], xf[D][TM];
+    float xv[D][TM];
+    // Loads of this wave's it-th K block into ring slot `slot`.  Blocks past
+    // the end issue the same instructions on an empty range (no traffic), so
+    // every step issues LPB loads and the waits below are fixed counts.
+    auto load = [&](int slot, int it) {
+        const bool live = it < nk;
+        const int kb = live ? (int)(wave + (int64_t)it * NW) : 0;
+        const __amdgpu_buffer_rsrc_t w_ = live ? wr : none, x_ = live ? xr : none, s_ = live ? sr : none;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int so = kb * BK + (int)(j * 16 * K);
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(w_, loff, so, 0);
+            const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(w_, loff + 16, so, 0);
+            wf[slot][j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        // (the X row of a lane is in the per-lane offset, so a row past M
+        // is out of range however the hardware counts the scalar offset)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int vo = loff + (int)(i * 16 * K);
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(x_, vo, kb * BK, 0);
+            const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(x_, vo + 16, kb * BK, 0);
+            xf[slot][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            xv[slot][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                        s_, soff + (int)(i * 16 * KB * 4), kb * 4, 0));
+        }
+    };
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        load(d, d);
+    for (int base = 0; base < nk; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int it = base + d;
+            wait_vmcnt<(D - 1) * LPB>(); // block `it` landed; D - 1 younger blocks may fly
+            if (it < nk) {
+                const float sw = ws_row[wave + (int64_t)it * NW];
+                float sc[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    sc[i] = xv[d][i] * sw;
+                v4f part[2];
+#pragma unroll
+                for (int t = 0; t < TM * TN; ++t) {
+                    const int i = t % TM, j = t / TM;
+                    part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[d][j], xf[d][i],
+                                                                                   v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                                   0, 127, 0, 127);
+                    if (t > 0) {
+                        const int pi = (t - 1) % TM, pj = (t - 1) / TM;
+                        acc[pi][pj] = __builtin_elementwise_fma(v4f{sc[pi], sc[pi], sc[pi], sc[pi]},
+                                                                part[(t - 1) & 1], acc[pi][pj]);
+                    }
+                }
+                constexpr int T = TM * TN;
+                acc[TM - 1][TN - 1] = __builtin_elementwise_fma(v4f{sc[TM - 1], sc[TM - 1], sc[TM - 1], sc[TM - 1]},
+                                                                part[(T - 1) & 1], acc[TM - 1][TN - 1]);
+            }
+            load(d, it + D);
+        }
+    }
+    wait_vmcnt<0>();
+
+    // ---- sum the 8 waves' partial tiles (wave order) and store ----
+    // lane holds Y[m = 16 i + fr][n = 16 j + 4 fg .. + 3] of its partial tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            *(v4f *)&red[wave][i * 16 + fr][j * 16 + fg * 4] = acc[i][j];
+    __syncthreads();
+    constexpr int GROUPS = TM * 16 * TN * 4; // 4-column groups of the tile
+    for (int g = threadIdx.x; g < GROUPS; g += NW * 64) {
+        const int m = g / (TN * 4), n = (g % (TN * 4)) * 4;
+        v4f v = *(const v4f *)&red[0][m][n];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            v += *(const v4f *)&red[w][m][n];
+        if (m < mrows) {
+            const int64_t row = m0 + m, col = n0 + n;
+            if (OUT_F32) {
+                *(v4f *)((float *)a.y + row * N + col) = v;
+            } else {
+                typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
+                const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
+                *(u32x2 *)((uint16_t *)a.y + row * N + col) =
+                    u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+            }
+        }
+    }
+}
+
 // ---- variant table -----------------------------------------------------------------
 //
 // A shape picks its kernel from (M, N, K) alone -- never from out_dtype -- so
@@ -742,6 +884,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 // constraints allow, for measurements.
 
 enum Variant { V_AUTO = 0, V_SIMPLE = 1, V_DMA = 2, V_DMA8 = 3 };
+// (V_AUTO also picks the weight-streaming kernel for few rows)
 
 static int forced_variant()
 {
@@ -792,6 +935,54 @@ static bool dma_ok(int64_t rows, int64_t N, int64_t K)
     return N % 256 == 0 && 256 * K < ((int64_t)1 << 32) && 256 * N * 4 < ((int64_t)1 << 31) && rows >= 128;
 }
 
+// The weight-streaming kernel: at most 128 activation rows, N a multiple of
+// 16, 32-bit buffer offsets (16 rows of K bytes per tile group, 128 rows of
+// X), and enough K blocks for the waves to share.
+static bool skinny_ok(int64_t M, int64_t N, int64_t K)
+{
+    return M <= 256 && N % 16 == 0 && 128 * K < ((int64_t)1 << 31) && K / 128 >= 8;
+}
+
+template <int TM, int TN, int D>
+static hipError_t run_skinny_t(GemmArgs a, bool out_f32, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(a.N / (TN * 16)), (unsigned)((a.M + TM * 16 - 1) / (TM * 16)));
+    if (out_f32)
+        return launch(gemm_skinny_kernel<TM, TN, D, true>, grid, dim3(512), 0, stream, a);
+    return launch(gemm_skinny_kernel<TM, TN, D, false>, grid, dim3(512), 0, stream, a);
+}
+
+// W tile width: the widest of 64 / 32 / 16 rows that still gives at least 256
+// workgroups (one per CU), so W streams from every CU; X rows per workgroup:
+// the fewest 16-row tiles covering M, up to 64 rows per chunk (above that,
+// each chunk of X rows re-reads W: larger chunks would re-read X from L2 once
+// per 16-row W tile, which costs more).
+static hipError_t run_skinny(GemmArgs a, bool out_f32, hipStream_t stream)
+{
+    const int64_t M = a.M, N = a.N;
+    const int tn = (N % 64 == 0 && N / 64 >= 256) ? 4 : (N % 32 == 0 && N / 32 >= 256) ? 2 : 1;
+    const int tm = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    if (tm == 1) {
+        if (tn == 4)
+            return run_skinny_t<1, 4, 4>(a, out_f32, stream);
+        if (tn == 2)
+            return run_skinny_t<1, 2, 4>(a, out_f32, stream);
+        return run_skinny_t<1, 1, 6>(a, out_f32, stream);
+    }
+    if (tm == 2) {
+        if (tn == 4)
+            return run_skinny_t<2, 4, 3>(a, out_f32, stream);
+        if (tn == 2)
+            return run_skinny_t<2, 2, 4>(a, out_f32, stream);
+        return run_skinny_t<2, 1, 4>(a, out_f32, stream);
+    }
+    if (tn == 4)
+        return run_skinny_t<4, 4, 2>(a, out_f32, stream);
+    if (tn == 2)
+        return run_skinny_t<4, 2, 3>(a, out_f32, stream);
+    return run_skinny_t<4, 1, 4>(a, out_f32, stream);
+}
+
 size_t gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
 
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
@@ -809,6 +1000,8 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     a.N = N;
     a.K = K;
     const int fv = forced_variant();
+    if (fv == V_AUTO && skinny_ok(M, N, K))
+        return run_skinny(a, out_fp32 != 0, stream);
     if (fv != V_SIMPLE && fv != V_DMA && dma_ok(M, N, K) && M >= 256) {
         a.tiles_m = (int)((M + 255) / 256);
         a.tiles_n = (int)(N / 256);

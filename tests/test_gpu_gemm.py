@@ -42,6 +42,10 @@ def _run_pair(fp8bs, orc, M, N, K, mode, seed_sub=0):
 SMALL = [
     (256, 512, 512),    # tiny layer
     (1, 128, 128), (17, 256, 384), (129, 384, 640), (300, 128, 1024), (127, 640, 256), (513, 1024, 1152),
+    # few-row shapes of the weight-streaming path: 1 / 2 / 4 / 8 sixteen-row X tiles (ragged M, two
+    # X-row chunks at M = 256), 16 / 32 / 64-row W tiles, K blocks not a multiple of the 8 waves
+    (1, 256, 1024), (5, 512, 2048), (16, 1024, 1152), (24, 16384, 1024), (33, 512, 1024), (64, 2048, 1280),
+    (100, 384, 2048), (256, 128, 1024), (7, 8192, 1024),
 ]
 
 
