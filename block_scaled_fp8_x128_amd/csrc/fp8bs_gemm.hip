@@ -1034,8 +1034,13 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
     a.N = N;
     a.K = K;
     a.E = E;
-    a.tiles_m = (int)((M_total + 127) / 128 + E);
     const int fv = forced_variant();
+    if (fv != V_SIMPLE && fv != V_DMA && dma_ok(M_total, N, K)) {
+        a.tiles_m = (int)((M_total + 255) / 256 + E);
+        a.tiles_n = (int)(N / 256);
+        return run_dma<256, 256, 4, 2, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    }
+    a.tiles_m = (int)((M_total + 127) / 128 + E);
     if (fv != V_SIMPLE && dma_ok(M_total, N, K)) {
         a.tiles_n = (int)(N / 256);
         return run_dma<128, 256, 2, 4, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
