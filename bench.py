@@ -325,7 +325,9 @@ def moe_workload(fp8bs, dev, mode):
         w2q=torch.empty((E * H, F), dtype=torch.uint8, device=dev),
         w2s=torch.empty((E * H // 128, F // 128), dtype=torch.float32, device=dev),
         y1=torch.empty((Mt, 2 * F), dtype=torch.bfloat16, device=dev),
-        y2=torch.empty((Mt, H), dtype=torch.bfloat16, device=dev))
+        y2=torch.empty((Mt, H), dtype=torch.bfloat16, device=dev),
+        wk1=torch.empty(max(1, fp8bs.grouped_workspace_size(E, Mt, 2 * F, H)), dtype=torch.uint8, device=dev),
+        wk2=torch.empty(max(1, fp8bs.grouped_workspace_size(E, Mt, H, F)), dtype=torch.uint8, device=dev))
 
     def step(timer):
         maybe(timer, "quant_w_experts", lambda: fp8bs.quant_w_128x128_batched([w1, w2], mode,
@@ -334,10 +336,11 @@ def moe_workload(fp8bs, dev, mode):
         maybe(timer, "quant_act_gate_up", lambda: fp8bs.quant_act_1x128(x1, mode, out=(b["x1q"], b["x1s"])))
         maybe(timer, "grouped_gate_up", lambda: fp8bs.fp8_block_grouped_gemm(
             b["x1q"], b["x1s"], b["w1q"].view(E, 2 * F, H), b["w1s"].view(E, 2 * F // 128, H // 128), offs_d,
-            out=b["y1"]))
+            out=b["y1"], workspace=b["wk1"]))
         maybe(timer, "quant_act_down", lambda: fp8bs.quant_act_1x128(x2, mode, out=(b["x2q"], b["x2s"])))
         maybe(timer, "grouped_down", lambda: fp8bs.fp8_block_grouped_gemm(
-            b["x2q"], b["x2s"], b["w2q"].view(E, H, F), b["w2s"].view(E, H // 128, F // 128), offs_d, out=b["y2"]))
+            b["x2q"], b["x2s"], b["w2q"].view(E, H, F), b["w2s"].view(E, H // 128, F // 128), offs_d, out=b["y2"],
+            workspace=b["wk2"]))
 
     shapes = {"gate_up": (Mt, 2 * F, H), "down": (Mt, H, F)}
     flops = sum(2.0 * m * n * k for m, n, k in shapes.values())

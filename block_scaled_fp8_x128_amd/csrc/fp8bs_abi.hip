@@ -176,11 +176,9 @@ size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K)
 
 size_t fp8bs_grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K)
 {
-    (void)E;
-    (void)M_total;
-    (void)N;
-    (void)K;
-    return 0;
+    if (E <= 0 || M_total <= 0 || N <= 0 || K <= 0)
+        return 0;
+    return fp8bs::grouped_workspace_size(E, M_total, N, K);
 }
 
 int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
@@ -208,8 +206,6 @@ int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, cons
                            const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
                            int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     int st = check_gemm_common(xq, xs, y, M_total, N, K, out_dtype);
     if (st != FP8BS_OK)
         return st;
@@ -222,10 +218,15 @@ int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, cons
         return FP8BS_INVALID_ARG;
     if ((M_total + 127) / 128 + E >= kMaxDim / (N / 128))
         return FP8BS_UNSUPPORTED_SHAPE;
+    const size_t need = fp8bs::grouped_workspace_size(E, M_total, N, K);
+    if (workspace_bytes < need)
+        return FP8BS_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+        return FP8BS_INVALID_ARG;
     if ((st = check_device()) != FP8BS_OK)
         return st;
     return status_of(fp8bs::launch_grouped_gemm(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y,
-                                                out_dtype == FP8BS_OUT_FP32, (hipStream_t)stream));
+                                                out_dtype == FP8BS_OUT_FP32, workspace, (hipStream_t)stream));
 }
 
 } // extern "C"

@@ -37,6 +37,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 namespace fp8bs {
 
 constexpr int BK = 128;        // K block = scale block
@@ -61,6 +63,14 @@ struct GemmCfg {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// One row tile of the grouped form: `rows` (1 .. BM) rows of expert e from
+// row_begin; e < 0 past the last tile.
+struct GroupTile {
+    int64_t row_begin;
+    int32_t e;
+    int32_t rows;
+};
+
 // Problem description shared by the dense and grouped launches.
 struct GemmArgs {
     const uint8_t *xq;
@@ -74,6 +84,9 @@ struct GemmArgs {
     int64_t E;              // grouped only
     int tiles_m;            // dense: ceil(M/BM); grouped: upper bound ceil(M_total/BM) + E
     int tiles_n;            // N / BN
+    int ksplit;             // persistent dense kernel: K ranges per output tile (1 = whole K)
+    float *part;            // ksplit > 1: fp32 partial sums [ksplit][M][N]
+    const GroupTile *gtab;  // grouped, persistent kernel: the row tiles (tiles_m entries)
 };
 
 // Logical tile of workgroup `bid` (XCD-contiguous ranges, GROUP_M swizzle).
@@ -137,6 +150,52 @@ __device__ __forceinline__ bool expert_of_tile(const int32_t *offsets, int64_t E
         prev_end = __shfl(end, 63);
     }
     return false;
+}
+
+// The row tiles of the grouped form, written once per launch by one wave so
+// that the GEMM workgroups look a tile up with one scalar load: expert e
+// contributes ceil(count_e / BM) tiles, in expert order; entries past the
+// last tile get e = -1.  Offsets are clamped and made non-decreasing as in
+// expert_of_tile.  tiles_m >= ceil(M_total / BM) + E bounds the count.
+template <int BM>
+__global__ __launch_bounds__(64) void grouped_tile_table_kernel(const int32_t *offsets, int64_t E, int64_t M_total,
+                                                                int tiles_m, GroupTile *tab)
+{
+    const int lane = threadIdx.x;
+    int64_t prev_end = offsets[0];
+    prev_end = prev_end < 0 ? 0 : (prev_end > M_total ? M_total : prev_end);
+    int base = 0;
+    for (int64_t e0 = 0; e0 < E; e0 += 64) {
+        const int64_t e = e0 + lane;
+        int64_t end = (e < E) ? (int64_t)offsets[e + 1] : prev_end;
+        end = end < prev_end ? prev_end : (end > M_total ? M_total : end);
+        for (int d = 1; d < 64; d <<= 1) { // inclusive max-scan
+            const int64_t o = __shfl_up(end, d);
+            if (lane >= d && o > end)
+                end = o;
+        }
+        int64_t start = __shfl_up(end, 1);
+        if (lane == 0)
+            start = prev_end;
+        const int cnt = (e < E) ? (int)((end - start + BM - 1) / BM) : 0;
+        int inc = cnt;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(inc, d);
+            if (lane >= d)
+                inc += o;
+        }
+        const int first = base + inc - cnt;
+        for (int j = 0; j < cnt; ++j) {
+            const int t = first + j;
+            const int64_t r0 = start + (int64_t)j * BM;
+            if (t < tiles_m)
+                tab[t] = GroupTile{r0, (int32_t)e, (int32_t)((end - r0) < BM ? (end - r0) : BM)};
+        }
+        base += __shfl(inc, 63);
+        prev_end = __shfl(end, 63);
+    }
+    for (int t = base + lane; t < tiles_m; t += 64)
+        tab[t] = GroupTile{0, -1, 0};
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
@@ -380,27 +439,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
-// Geometry of one output tile of the persistent kernels.
+// Geometry of one work unit of the persistent kernels: an output tile and
+// the range of K blocks it sums (the whole of K unless the product is split
+// along K).
 struct TileGeo {
     int64_t row_begin, row_end; // rows of X / Y: [row_begin, row_end)
     int64_t n0;                 // first column of Y (row of W)
     const uint8_t *wq;          // this tile's weight matrix (the expert's, for the grouped form)
     const float *ws;
+    int kb0, kb1;               // K blocks [kb0, kb1)
+    int ks;                     // index of the K range (0 .. ksplit - 1)
 };
 
-// Tile of virtual id v (< tiles_m * tiles_n), or false for a grouped tile
-// past the last row tile of its expert list.
-template <int BM, int BN, bool GROUPED>
-__device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int ntiles, TileGeo &g)
+// Work unit of virtual id v (< tiles_m * tiles_n * ksplit), or false for a
+// grouped tile past the last row tile of its expert list.  Units are spread
+// XCD-contiguously; the K range is the slowest index, so the units resident
+// on one XCD share the same K slice of both operands.
+template <int BM, int BN, bool GROUPED, bool SPLIT>
+__device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, TileGeo &g)
 {
+    if (nunits % NUM_XCD == 0)
+        v = (v % NUM_XCD) * (nunits / NUM_XCD) + v / NUM_XCD;
+    const int KB = (int)(a.K / BK);
+    if (SPLIT) {
+        const int ntl = a.tiles_m * a.tiles_n;
+        const int ks = v / ntl;
+        v -= ks * ntl;
+        g.ks = ks;
+        g.kb0 = (int)((int64_t)ks * KB / a.ksplit);
+        g.kb1 = (int)((int64_t)(ks + 1) * KB / a.ksplit);
+    } else {
+        g.ks = 0;
+        g.kb0 = 0;
+        g.kb1 = KB;
+    }
     int tm, tn;
-    tile_of(v, ntiles, a.tiles_m, a.tiles_n, tm, tn);
+    tile_of(v, 1, a.tiles_m, a.tiles_n, tm, tn); // (grid 1: no second XCD remap)
     g.wq = a.wq;
     g.ws = a.ws;
     if (GROUPED) {
-        int e;
-        if (!expert_of_tile<BM>(a.offsets, a.E, a.M, tm, e, g.row_begin, g.row_end))
+        const CONST_AS GroupTile *d = (const CONST_AS GroupTile *)a.gtab + tm;
+        const int e = d->e;
+        if (e < 0)
             return false;
+        g.row_begin = d->row_begin;
+        g.row_end = g.row_begin + d->rows;
         g.wq += (int64_t)e * a.N * a.K;
         g.ws += (int64_t)e * (a.N / 128) * (a.K / BK);
     } else {
@@ -419,11 +502,15 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int ntiles, T
 // fragments of step s + 1 are read into registers during the last MFMA
 // groups of step s, so the matrix cores never wait on LDS at a step
 // boundary; a tile's output stores drain while the next tile computes.  Stores are buffer stores
-// whose out-of-range rows the hardware drops.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
+// whose out-of-range rows the hardware drops.  SPLIT: the work units are
+// (tile, K range) pairs and each writes its fp32 partial tile to the
+// partial-sum buffer (ksplit slices of M x N), summed by splitk_reduce_kernel.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs a)
 {
-    using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>;
+    // three LDS stages (two steps of loads in flight) where they fit
+    constexpr int NST = 3 * DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>::STAGE_BYTES <= 160 * 1024 ? 3 : 2;
+    using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, NST>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::STAGES * C::STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -431,7 +518,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WAVES_M, wn = wave / WAVES_M;
     const int64_t K = a.K, KB = K / BK, N = a.N;
-    const int ntiles = a.tiles_m * a.tiles_n;
+    const int ntiles = a.tiles_m * a.tiles_n * (SPLIT ? a.ksplit : 1); // work units
     const int sub = lane >> 3, slot = lane & 7;
     const int fr = lane & 15, fg = lane >> 4;
 
@@ -439,12 +526,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     int dv = blockIdx.x;
     TileGeo dt;
     bool dvalid = false;
-    while (dv < ntiles && !(dvalid = tile_geo<BM, BN, GROUPED>(a, dv, ntiles, dt)))
+    while (dv < ntiles && !(dvalid = tile_geo<BM, BN, GROUPED, SPLIT>(a, dv, ntiles, dt)))
         dv += gridDim.x;
     if (!dvalid)
         return; // no tile for this workgroup (uniform)
     TileGeo ct = dt; // tile of the step being computed
-    int64_t dkb = 0;
+    int cv = dv;     // ... and its virtual id
+    int64_t dkb = dt.kb0;
 
     // ---- per-tile DMA state ----
     // Row group t of a wave (LDS rows 8 (wave + NW t) .. + 7) holds tile rows
@@ -456,56 +544,72 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // never stored); the activation scales are bounded the same way.  Offsets
     // are 32-bit (the launcher only picks this kernel when 256 K < 2^32).
     constexpr int GROW = 8 * C::NW; // rows between a wave's consecutive row groups
-    // (the resources are rebuilt per issue from the tile's bases and row
-    // count: the host pass of this compiler emits no launch stub for a kernel
-    // holding an array of buffer resources)
+    // (the resources are rebuilt per issue from the tile's bases and byte
+    // counts, which are computed once per tile: the host pass of this
+    // compiler emits no launch stub for a kernel holding an array of buffer
+    // resources)
     const uint8_t *xbase, *wbase;
     const float *sbase;
-    int64_t xrows;
+    uint32_t xnr[C::XG]; // bytes of X in row group t (0 past the tile's last row)
+    uint32_t snr;        // bytes of the tile's activation-scale rows
     const int r0 = tile_row(wave * 8 + sub);
     const uint32_t loff = (uint32_t)(r0 * K) + (uint32_t)((slot ^ (r0 & 7)) << 4);
     const uint32_t soff = (uint32_t)((wm * C::WM + lane) * KB * 4);
     auto dma_setup = [&](const TileGeo &g) {
         xbase = a.xq + g.row_begin * K;
-        xrows = g.row_end - g.row_begin;
         wbase = g.wq + g.n0 * K;
         sbase = a.xs + g.row_begin * KB;
-    };
-    // Loads of K block kb into `stage`.  With live == false every range is
-    // empty, so the same instructions move nothing (the hardware range check
-    // drops them): the caller issues them unconditionally, keeping the MFMA
-    // stream they sit in free of branches.
-    auto issue = [&](int64_t kb, int stage, bool live = true) {
-        uint8_t *L = lds + stage * C::STAGE_BYTES;
-        const int ko = (int)(kb * BK);
-        const int64_t rows = live ? xrows : 0;
+        const int64_t rows = g.row_end - g.row_begin; // 1 .. BM
 #pragma unroll
         for (int t = 0; t < C::XG; ++t) {
             const int64_t left = rows - (int64_t)GROW * t;
-            const __amdgpu_buffer_rsrc_t xr = make_rsrc(xbase + (int64_t)GROW * t * K, left > 0 ? left * K : 0);
+            xnr[t] = left > 0 ? (uint32_t)(left * K) : 0u;
+        }
+        snr = (uint32_t)(rows * KB * 4);
+    };
+    // Load q (0 .. DPW - 1) of K block kb into `stage`: X row groups, then W
+    // row groups, then the activation scales.  With live == false every
+    // range is empty, so the same instructions move nothing (the hardware
+    // range check drops them): the caller issues them unconditionally,
+    // keeping the MFMA stream they sit in free of branches.
+    auto issue_q = [&](int q, int64_t kb, int stage, bool live) __attribute__((always_inline)) {
+        uint8_t *L = lds + stage * C::STAGE_BYTES;
+        const int ko = (int)(kb * BK);
+        if (q < C::XG) {
+            const int t = q;
+            const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(xbase + (int64_t)GROW * t * K), (short)0, (int)(live ? xnr[t] : 0u), 0x00020000);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (LDS_AS void *)(L + (wave + C::NW * t) * 1024), 16,
                                                      (int)loff, ko, 0, 0);
-        }
-        const __amdgpu_buffer_rsrc_t wl = make_rsrc(wbase, live ? (int64_t)BN * K : 0);
-#pragma unroll
-        for (int t = 0; t < C::WG; ++t)
+        } else if (q < C::XG + C::WG) {
+            const int t = q - C::XG;
+            const __amdgpu_buffer_rsrc_t wl = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(wbase), (short)0, live ? (int)(uint32_t)((int64_t)BN * K) : 0, 0x00020000);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wl, (LDS_AS void *)(L + BM * BK + (wave + C::NW * t) * 1024),
                                                      16, (int)loff, ko + (int)(GROW * t * K), 0, 0);
-        const __amdgpu_buffer_rsrc_t sl = make_rsrc(sbase, rows * KB * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sl, (LDS_AS void *)(L + C::XS_OFF + wave * 256), 4, (int)soff,
-                                                 (int)(kb * 4), 0, 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t sl = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(sbase), (short)0, (int)(live ? snr : 0u), 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sl, (LDS_AS void *)(L + C::XS_OFF + wave * 256), 4, (int)soff,
+                                                     (int)(kb * 4), 0, 0);
+        }
+    };
+    auto issue = [&](int64_t kb, int stage, bool live = true) {
+#pragma unroll
+        for (int q = 0; q < C::DPW; ++q)
+            issue_q(q, kb, stage, live);
     };
     // advance the DMA cursor by one K block; false at the end of the stream
     auto dma_next = [&]() {
-        if (++dkb < KB)
+        if (++dkb < dt.kb1)
             return true;
-        dkb = 0;
         do {
             dv += gridDim.x;
-        } while (dv < ntiles && !tile_geo<BM, BN, GROUPED>(a, dv, ntiles, dt));
+        } while (dv < ntiles && !tile_geo<BM, BN, GROUPED, SPLIT>(a, dv, ntiles, dt));
         if (dv >= ntiles)
             return false;
         dma_setup(dt);
+        dkb = dt.kb0;
         return true;
     };
 
@@ -562,18 +666,22 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // MFMAs to land.  The rescale of MFMA tile t is issued after the MFMA of
     // tile t + 1, so the matrix core has the next product queued while the
     // VALU applies the previous one.  Before group TN - 2 every wave waits for
-    // the next step's operands (the most recent loads it issued) and for its
-    // own LDS reads (the last read of this stage was issued in group TN - 3),
-    // and passes the barrier: the next stage is then complete for all waves
-    // and no wave reads this stage any more, so the loads issued at the top of
-    // the next step may refill it.  Groups TN - 2 and TN - 1 then read the
-    // next step's first two W fragments and scales, and each MFMA of the last
-    // group frees its X fragment registers for the next step's.  (For the last
-    // step of a workgroup those reads fetch data that is never used; the
-    // barrier is uniform.)
-    auto compute = [&](int stage, float sw_next, auto &&after_barrier) __attribute__((always_inline)) {
+    // the next step's operands and for its own LDS reads (the last read of
+    // this stage was issued in group TN - 3), and passes the barrier: the next
+    // stage is then complete for all waves and no wave reads this stage any
+    // more, so the loads of a later step may refill it.  Those loads are
+    // spread over the MFMAs of groups TN - 2 and TN - 1 (issued in one block
+    // right after the barrier, where every wave of the CU is at the same
+    // point, they would leave the matrix cores idle while their addresses are
+    // formed).  Groups TN - 2 and TN - 1 also read the next step's first two
+    // W fragments and scales, and each MFMA of the last group frees its X
+    // fragment registers for the next step's.  (For the last step of a
+    // workgroup those reads fetch data that is never used; the barrier is
+    // uniform.)
+    auto compute = [&](int stage, int nstage, bool full_wait, float sw_next, auto &&load_q)
+                       __attribute__((always_inline)) {
         const uint8_t *L = lds + stage * C::STAGE_BYTES;
-        const uint8_t *Ln = lds + (stage ^ 1) * C::STAGE_BYTES;
+        const uint8_t *Ln = lds + nstage * C::STAGE_BYTES;
         v4f part[2];
         float xs_next[C::TM];
 #pragma unroll
@@ -582,10 +690,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             if (j + 2 < C::TN) {
                 awq[(j + 2) % 3] = frag(L + wo[0] + (j + 2) * 2048, L + wo[1] + (j + 2) * 2048);
             } else if (j + 2 == C::TN) {
-                wait_vmcnt<0>();
+                // the next step's loads have landed; those of the steps after
+                // it (issued later) may still fly.  The count also covers
+                // stores, which may complete out of order with the loads: in
+                // the first step after a tile's output stores, wait for all.
+                if (C::STAGES == 2 || full_wait)
+                    wait_vmcnt<0>();
+                else
+                    wait_vmcnt<(C::STAGES - 2) * C::DPW>();
                 wait_lgkmcnt0();
                 sync();
-                after_barrier();
                 awq[(j + 2) % 3] = frag(Ln + wo[0], Ln + wo[1]);
 #pragma unroll
                 for (int i = 0; i < C::TM; ++i)
@@ -603,24 +717,24 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 const int t = j * C::TM + i;
                 part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], v4f{0.f, 0.f, 0.f, 0.f},
                                                                                0, 0, 0, 127, 0, 127);
+                // issue order, fenced: each MFMA, then the rescale of the
+                // previous one (whose product has had a full MFMA to land),
+                // and in the last group the next step's X fragment it freed;
+                // after the barrier, the next loads one or two per MFMA
+                __builtin_amdgcn_sched_barrier(0);
                 if (t > 0)
                     rescale(t - 1, part[(t - 1) & 1]);
                 if (last)
                     bx[i] = frag(Ln + xo[0] + i * 2048, Ln + xo[1] + i * 2048);
-            }
-            // issue order: each MFMA followed by the previous rescale (and in
-            // the last group by the next step's X fragment it freed)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                if (j + 2 >= C::TN) {
+                    const int slot_i = (j + 2 - C::TN) * C::TM + i;
 #pragma unroll
-            for (int i = 1; i < C::TM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (last)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    for (int q = 0; q < C::DPW; ++q)
+                        if (q * 2 * C::TM / C::DPW == slot_i)
+                            load_q(q);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (last)
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         rescale(C::TM * C::TN - 1, part[(C::TM * C::TN - 1) & 1]);
 #pragma unroll
@@ -633,12 +747,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         awq[1] = n1;
     };
 
-    // Output of a finished tile: buffer stores over the tile's own rows, so
-    // rows past row_end are dropped by the range check, not by a branch.
-    auto epilogue = [&](const TileGeo &g) {
-        constexpr int ES = OUT_F32 ? 4 : 2;
+    // Output of a finished work unit: buffer stores over the tile's own rows,
+    // so rows past row_end are dropped by the range check, not by a branch.
+    // A unit that sums one K range of a split product writes its fp32
+    // partial tile to slice ks of the partial-sum buffer instead.
+    auto store = [&](auto f32_tag, const uint8_t *base, const TileGeo &g) {
+        constexpr bool F32 = decltype(f32_tag)::value;
+        constexpr int ES = F32 ? 4 : 2;
         const __amdgpu_buffer_rsrc_t yr =
-            make_rsrc((const uint8_t *)a.y + (g.row_begin * N + g.n0) * ES, (g.row_end - g.row_begin) * N * ES);
+            make_rsrc(base + (g.row_begin * N + g.n0) * ES, (g.row_end - g.row_begin) * N * ES);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
             const int m = wm * C::WM + i * 16 + fr;
@@ -647,7 +764,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 const int n = wn * C::WN + j * 16 + fg * 4;
                 const int off = (int)(((int64_t)m * N + n) * ES);
                 const v4f v = acc[i][j];
-                if (OUT_F32) {
+                if constexpr (F32) {
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yr, off, 0, 0);
                 } else {
                     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -660,15 +777,41 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             }
         }
     };
+    auto epilogue = [&](const TileGeo &g) {
+        if constexpr (SPLIT)
+            store(std::true_type{}, (const uint8_t *)(a.part + (int64_t)g.ks * a.M * N), g);
+        else
+            store(std::integral_constant<bool, OUT_F32>{}, (const uint8_t *)a.y, g);
+    };
 
-    // prologue: the first step's operands, fragments and scales
+    // Pipeline.  While step s is computed from stage s % STAGES, the loads of
+    // steps s + 1 .. s + STAGES - 1 are in flight (or landed) in the other
+    // stages; those of step s + STAGES are issued right after the barrier in
+    // the middle of step s, the earliest point at which every wave has
+    // finished reading the stage they refill.  Every pipeline slot issues its
+    // loads -- on empty ranges past the end of the stream -- so the wait
+    // counts stay exact.  Per step in flight only a flag and the address of
+    // its weight scale are carried; the tile of the step being computed
+    // advances with its own cursor.
+    // prologue: steps 0 .. STAGES - 2 issued, step 0's fragments and scales read
     dma_setup(dt);
-    issue(0, 0);
+    issue(dkb, 0);
     bool dmore = dma_next();
-    wait_vmcnt<0>();
+    const bool has1_0 = dmore;
+    const CONST_AS float *wsp1_0 = has1_0 ? ws_of(dt) + dkb : ws_of(ct) + ct.kb0;
+    bool has2 = false; // (three stages) step s + 2 exists
+    const CONST_AS float *wsp2 = wsp1_0;
+    if constexpr (C::STAGES == 3) {
+        issue(dkb, 1, has1_0);
+        if (has1_0)
+            dmore = dma_next();
+        has2 = has1_0 && dmore;
+        wsp2 = has2 ? ws_of(dt) + dkb : wsp1_0;
+    }
+    wait_vmcnt<(C::STAGES - 2) * C::DPW>();
     sync();
     {
-        const float sw = ws_of(ct)[0];
+        const float sw = ws_of(ct)[ct.kb0];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
             sc[i] = *(const float *)(lds + so + i * 64) * sw;
@@ -678,25 +821,20 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         awq[0] = frag(lds + wo[0], lds + wo[1]);
         awq[1] = frag(lds + wo[0] + 2048, lds + wo[1] + 2048);
     }
-
-    // Lookahead: the operands of step s + 1 are in flight (or landed) while
-    // step s is computed; those of step s + 2 are issued right after the
-    // barrier in the middle of step s, the earliest point at which every wave
-    // has finished reading the stage they refill.  Per lookahead step only a
-    // flag and the address of its weight scale are carried; the tile of the
-    // step being computed advances with its own cursor.
-    int cv = dv;
-    bool has1 = dmore;
-    const CONST_AS float *wsp1 = ws_of(ct);
-    if (has1) {
-        wsp1 = ws_of(dt) + dkb;
-        issue(dkb, 1);
-        dmore = dma_next();
+    bool has1 = has1_0;
+    const CONST_AS float *wsp1 = wsp1_0;
+    {
+        // the last slot: step STAGES - 1 into stage STAGES - 1
+        const bool hl = C::STAGES == 3 ? has2 : has1;
+        issue(dkb, C::STAGES - 1, hl);
+        if (hl)
+            dmore = dma_next();
     }
 
     int stage = 0;
-    int64_t ckb = 0;
+    int64_t ckb = ct.kb0;
     bool advance = false; // the cursor's step was issued during the previous step
+    bool stored = false;  // the previous step ended with a tile's output stores
     while (true) {
         if (advance)
             dmore = dma_next();
@@ -709,28 +847,38 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             // which would also wait for the fragment reads issued ahead.
             asm volatile("" ::"s"(sw_next));
         }
-        const bool has2 = dmore;
-        const int64_t kb2 = dkb;
-        const CONST_AS float *wsp2 = has2 ? ws_of(dt) + dkb : wsp1;
+        const bool hasS = dmore; // step s + STAGES exists
+        const int64_t kbS = dkb;
+        const CONST_AS float *wspS = hasS ? ws_of(dt) + dkb : (C::STAGES == 3 ? wsp2 : wsp1);
+        const int nstage = stage + 1 == C::STAGES ? 0 : stage + 1;
         // only the loads go in the middle of the MFMA stream; the cursor
         // advances (and sets up the next tile's loads) at the top of the
         // next step
-        compute(stage, sw_next, [&]() { issue(kb2, stage, has2); });
-        advance = has2;
-        stage ^= 1;
-        if (++ckb == KB) {
+        compute(stage, nstage, stored, sw_next, [&](int q) { issue_q(q, kbS, stage, hasS); });
+        advance = hasS;
+        stage = nstage;
+        stored = false;
+        if (++ckb == ct.kb1) {
             epilogue(ct);
-            ckb = 0;
+            stored = true;
             if (has1) {
                 do {
                     cv += gridDim.x;
-                } while (!tile_geo<BM, BN, GROUPED>(a, cv, ntiles, ct));
+                } while (!tile_geo<BM, BN, GROUPED, SPLIT>(a, cv, ntiles, ct));
+                ckb = ct.kb0;
             }
         }
         if (!has1)
             break;
-        has1 = has2;
-        wsp1 = wsp2;
+        if constexpr (C::STAGES == 3) {
+            has1 = has2;
+            wsp1 = wsp2;
+            has2 = hasS;
+            wsp2 = wspS;
+        } else {
+            has1 = hasS;
+            wsp1 = wspS;
+        }
     }
 }
 
@@ -876,15 +1024,40 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
     }
 }
 
+// ---- split-K reduction ----------------------------------------------------------
+//
+// Y = sum over the K ranges of the fp32 partial tiles, added in K-range order
+// (a fixed order, so results are deterministic), four columns per thread.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, void *__restrict__ y,
+                                                            int64_t MN, int ksplit)
+{
+    const int64_t n4 = MN / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        v4f v = *(const v4f *)(part + i * 4);
+        for (int s = 1; s < ksplit; ++s)
+            v += *(const v4f *)(part + s * MN + i * 4);
+        if (OUT_F32) {
+            *(v4f *)((float *)y + i * 4) = v;
+        } else {
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
+            const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
+            *(u32x2 *)((uint16_t *)y + i * 4) = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        }
+    }
+}
+
 // ---- variant table -----------------------------------------------------------------
 //
 // A shape picks its kernel from (M, N, K) alone -- never from out_dtype -- so
 // the fp32 and bf16 outputs of one shape come from the same arithmetic.
-// FP8BS_GEMM_VARIANT=simple|dma (read once) forces a kernel where its shape
-// constraints allow, for measurements.
+// For measurements, FP8BS_GEMM_VARIANT=simple|dma|dma8|skinny forces a kernel
+// where its shape constraints allow (dma: 128 x 256 tiles, dma8: 256 x 256)
+// and FP8BS_GEMM_KSPLIT=n the number of K ranges of the persistent dense
+// kernel; both are read once per process.
 
-enum Variant { V_AUTO = 0, V_SIMPLE = 1, V_DMA = 2, V_DMA8 = 3 };
-// (V_AUTO also picks the weight-streaming kernel for few rows)
+enum Variant { V_AUTO = 0, V_SIMPLE = 1, V_DMA = 2, V_DMA8 = 3, V_SKINNY = 4 };
 
 static int forced_variant()
 {
@@ -898,7 +1071,19 @@ static int forced_variant()
             return (int)V_DMA;
         if (!strcmp(e, "dma8"))
             return (int)V_DMA8;
+        if (!strcmp(e, "skinny"))
+            return (int)V_SKINNY;
         return (int)V_AUTO;
+    }();
+    return v;
+}
+
+static int forced_ksplit()
+{
+    static const int v = [] {
+        const char *e = getenv("FP8BS_GEMM_KSPLIT");
+        const int n = e ? atoi(e) : 0;
+        return n > 0 ? n : 0;
     }();
     return v;
 }
@@ -912,36 +1097,60 @@ static hipError_t run_simple(GemmArgs a, int grid, bool out_f32, hipStream_t str
     return launch(gemm_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED>, dim3(grid), block, 0, stream, a);
 }
 
-// Persistent launch: one workgroup per CU (at most one tile per workgroup
-// when there are fewer tiles than CUs); the count is a multiple of the 8
-// XCDs so that tile_of's XCD-contiguous ranges line up with the dispatch.
+// Persistent launch: one workgroup per CU (at most one work unit per
+// workgroup when there are fewer units than CUs); the count is a multiple of
+// the 8 XCDs so that the XCD-contiguous unit ranges line up with the dispatch.
 constexpr int kPersistentGrid = 256;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED>
-static hipError_t run_dma(GemmArgs a, int ntiles, bool out_f32, hipStream_t stream)
+static hipError_t run_dma(GemmArgs a, bool out_f32, hipStream_t stream)
 {
     const dim3 block(WAVES_M * WAVES_N * 64);
-    const int grid = ntiles < kPersistentGrid ? ntiles : kPersistentGrid;
-    if (out_f32)
-        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED>, dim3(grid), block, 0, stream, a);
-    return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED>, dim3(grid), block, 0, stream, a);
+    const int units = a.tiles_m * a.tiles_n * a.ksplit;
+    const int grid = units < kPersistentGrid ? units : kPersistentGrid;
+    if (GROUPED || a.ksplit == 1) {
+        if (out_f32)
+            return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED, false>, dim3(grid), block, 0, stream,
+                          a);
+        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED, false>, dim3(grid), block, 0, stream, a);
+    }
+    if constexpr (!GROUPED) { // (the grouped form is never split)
+        const hipError_t e =
+            launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, true>, dim3(grid), block, 0, stream, a);
+        if (e != hipSuccess)
+            return e;
+        const int64_t MN = a.M * a.N;
+        int64_t rb = (MN / 4 + 255) / 256;
+        rb = rb < 4096 ? rb : 4096;
+        if (out_f32)
+            return launch(splitk_reduce_kernel<true>, dim3((unsigned)rb), dim3(256), 0, stream, (const float *)a.part,
+                          a.y, MN, a.ksplit);
+        return launch(splitk_reduce_kernel<false>, dim3((unsigned)rb), dim3(256), 0, stream, (const float *)a.part, a.y,
+                      MN, a.ksplit);
+    }
+    return hipErrorInvalidValue;
 }
 
 // The large-tile kernels: N a multiple of their 256-wide tile, 32-bit
 // LDS-DMA offsets (256 rows of K bytes) and 32-bit store offsets (256 rows of
-// N fp32), and enough rows for 128-row tiles to be worth it.
-static bool dma_ok(int64_t rows, int64_t N, int64_t K)
+// N fp32).
+static bool dma_ok(int64_t N, int64_t K)
 {
-    return N % 256 == 0 && 256 * K < ((int64_t)1 << 32) && 256 * N * 4 < ((int64_t)1 << 31) && rows >= 128;
+    return N % 256 == 0 && 256 * K < ((int64_t)1 << 32) && 256 * N * 4 < ((int64_t)1 << 31);
 }
 
-// The weight-streaming kernel: at most 128 activation rows, N a multiple of
+// The weight-streaming kernel: at most 256 activation rows, N a multiple of
 // 16, 32-bit buffer offsets (16 rows of K bytes per tile group, 128 rows of
 // X), and enough K blocks for the waves to share.
 static bool skinny_ok(int64_t M, int64_t N, int64_t K)
 {
     return M <= 256 && N % 16 == 0 && 128 * K < ((int64_t)1 << 31) && K / 128 >= 8;
 }
+
+// Rows up to which the weight-streaming kernel is the automatic choice (above
+// them the persistent kernel, split along K where it has few tiles, is faster
+// on the decode shapes).
+constexpr int64_t kSkinnyMaxM = 16;
 
 template <int TM, int TN, int D>
 static hipError_t run_skinny_t(GemmArgs a, bool out_f32, hipStream_t stream)
@@ -983,10 +1192,74 @@ static hipError_t run_skinny(GemmArgs a, bool out_f32, hipStream_t stream)
     return run_skinny_t<4, 1, 4>(a, out_f32, stream);
 }
 
-size_t gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
+// Number of K ranges for a persistent launch of `tiles` output tiles over KB
+// K blocks: the split that minimizes the rounds of units per CU times the
+// steps of a unit (plus a per-unit and a reduction overhead, in K-step units),
+// with at least four K blocks per range.  Large products (tiles >= CUs) stay
+// unsplit.
+static int choose_ksplit(int64_t tiles, int64_t KB)
+{
+    if (tiles >= kPersistentGrid)
+        return 1;
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int ks = 1; ks <= 32 && KB / ks >= 4; ++ks) {
+        const int64_t rounds = (tiles * ks + kPersistentGrid - 1) / kPersistentGrid;
+        const int64_t cost = rounds * ((KB + ks - 1) / ks + 2) + (ks > 1 ? 2 : 0);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = ks;
+        }
+    }
+    return best;
+}
+
+enum Kind { K_SIMPLE, K_DMA128, K_DMA256, K_SKINNY };
+struct Plan {
+    int kind;
+    int tiles_m, tiles_n, ksplit;
+};
+
+// The kernel, tiling and K split of a dense product: a function of the shape
+// (and the measurement overrides) only, shared by the workspace query and
+// the launch.
+static Plan plan_dense(int64_t M, int64_t N, int64_t K)
+{
+    const int fv = forced_variant();
+    const int64_t KB = K / BK;
+    Plan p = {K_SIMPLE, (int)((M + 127) / 128), (int)(N / 128), 1};
+    if (skinny_ok(M, N, K) && ((fv == V_AUTO && M <= kSkinnyMaxM) || fv == V_SKINNY)) {
+        p.kind = K_SKINNY;
+        return p;
+    }
+    if (fv == V_SIMPLE || !dma_ok(N, K))
+        return p;
+    // 256 x 256 tiles when they fill every CU at least once, else 128 x 256
+    const bool big = fv == V_DMA8 || (fv != V_DMA && ((M + 255) / 256) * (N / 256) >= kPersistentGrid);
+    const int bm = big ? 256 : 128;
+    p.kind = big ? K_DMA256 : K_DMA128;
+    p.tiles_m = (int)((M + bm - 1) / bm);
+    p.tiles_n = (int)(N / 256);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    int ks = forced_ksplit() ? forced_ksplit() : choose_ksplit(tiles, KB);
+    ks = ks < (int)KB ? ks : (int)KB;
+    // units are counted in int; a split product's partial sums stay addressable
+    while (ks > 1 && tiles * ks > (1 << 30))
+        --ks;
+    p.ksplit = ks;
+    return p;
+}
+
+size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    const Plan p = plan_dense(M, N, K);
+    return p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
 
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
-                       int64_t K, void *y, int out_fp32, void *, hipStream_t stream)
+                       int64_t K, void *y, int out_fp32, void *workspace, hipStream_t stream)
 {
     if (M == 0)
         return hipSuccess;
@@ -999,27 +1272,42 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     a.M = M;
     a.N = N;
     a.K = K;
-    const int fv = forced_variant();
-    if (fv == V_AUTO && skinny_ok(M, N, K))
+    const Plan p = plan_dense(M, N, K);
+    a.tiles_m = p.tiles_m;
+    a.tiles_n = p.tiles_n;
+    a.ksplit = p.ksplit;
+    a.part = (float *)workspace;
+    switch (p.kind) {
+    case K_SKINNY:
         return run_skinny(a, out_fp32 != 0, stream);
-    if (fv != V_SIMPLE && fv != V_DMA && dma_ok(M, N, K) && M >= 256) {
-        a.tiles_m = (int)((M + 255) / 256);
-        a.tiles_n = (int)(N / 256);
-        return run_dma<256, 256, 4, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+    case K_DMA256:
+        return run_dma<256, 256, 4, 2, false>(a, out_fp32 != 0, stream);
+    case K_DMA128:
+        return run_dma<128, 256, 2, 4, false>(a, out_fp32 != 0, stream);
+    default:
+        return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
     }
-    if (fv != V_SIMPLE && dma_ok(M, N, K)) {
-        a.tiles_m = (int)((M + 127) / 128);
-        a.tiles_n = (int)(N / 256);
-        return run_dma<128, 256, 2, 4, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
-    }
-    a.tiles_m = (int)((M + 127) / 128);
-    a.tiles_n = (int)(N / 128);
-    return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+}
+
+// Row tiles of the grouped form's persistent kernels (the table's length):
+// BM = 256 unless forced to 128.
+static int64_t grouped_tiles_m(int64_t E, int64_t M_total)
+{
+    const int fv = forced_variant();
+    const int64_t bm = (fv == V_DMA) ? 128 : 256;
+    return (M_total + bm - 1) / bm + E;
+}
+
+size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K)
+{
+    if (E <= 0 || M_total <= 0 || forced_variant() == V_SIMPLE || !dma_ok(N, K))
+        return 0;
+    return (size_t)grouped_tiles_m(E, M_total) * sizeof(GroupTile);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
-                               int out_fp32, hipStream_t stream)
+                               int out_fp32, void *workspace, hipStream_t stream)
 {
     if (M_total == 0)
         return hipSuccess;
@@ -1034,17 +1322,24 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
     a.N = N;
     a.K = K;
     a.E = E;
+    a.ksplit = 1;
     const int fv = forced_variant();
-    if (fv != V_SIMPLE && fv != V_DMA && dma_ok(M_total, N, K)) {
-        a.tiles_m = (int)((M_total + 255) / 256 + E);
+    if (grouped_workspace_size(E, M_total, N, K) > 0) {
+        a.tiles_m = (int)grouped_tiles_m(E, M_total);
         a.tiles_n = (int)(N / 256);
-        return run_dma<256, 256, 4, 2, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+        a.gtab = (const GroupTile *)workspace;
+        const bool big = fv != V_DMA;
+        hipError_t e = big ? launch(grouped_tile_table_kernel<256>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
+                                    a.tiles_m, (GroupTile *)workspace)
+                           : launch(grouped_tile_table_kernel<128>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
+                                    a.tiles_m, (GroupTile *)workspace);
+        if (e != hipSuccess)
+            return e;
+        if (big)
+            return run_dma<256, 256, 4, 2, true>(a, out_fp32 != 0, stream);
+        return run_dma<128, 256, 2, 4, true>(a, out_fp32 != 0, stream);
     }
     a.tiles_m = (int)((M_total + 127) / 128 + E);
-    if (fv != V_SIMPLE && dma_ok(M_total, N, K)) {
-        a.tiles_n = (int)(N / 256);
-        return run_dma<128, 256, 2, 4, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
-    }
     a.tiles_n = (int)(N / 128);
     return run_simple<128, 128, 2, 2, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
 }

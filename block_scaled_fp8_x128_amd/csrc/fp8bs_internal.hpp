@@ -47,8 +47,9 @@ hipError_t launch_quant_w(const WTensor *t, int64_t count, int mode, hipStream_t
 size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
                        int64_t K, void *y, int out_fp32, void *workspace, hipStream_t stream);
+size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
-                               int out_fp32, hipStream_t stream);
+                               int out_fp32, void *workspace, hipStream_t stream);
 
 } // namespace fp8bs

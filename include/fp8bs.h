@@ -142,9 +142,12 @@ FP8BS_API int quant_w_128x128_batched(int64_t count, const void *const *w_bf16, 
  * is the round-to-nearest-even of exactly the value the fp32 output holds.
  * A given (M, N, K) always runs the same kernel: results are deterministic.
  *
- *   workspace, workspace_bytes: device scratch for split-K partial sums of
- *   small-M shapes; fp8bs_gemm_workspace_size(M, N, K) gives the size needed
- *   (0 for most shapes, where workspace may be NULL).  It need not be zeroed.
+ *   workspace, workspace_bytes: device scratch for the fp32 partial sums of
+ *   products split along K (shapes with fewer 256-wide output tiles than the
+ *   GPU has compute units, e.g. decode-sized M): ksplit * M * N * 4 bytes,
+ *   as fp8bs_gemm_workspace_size(M, N, K) returns (0 for the other shapes,
+ *   where workspace may be NULL).  It need not be zeroed; its contents are
+ *   overwritten.  Two calls that share a workspace must not overlap in time.
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE (N or K not a multiple of 128),
  * WORKSPACE_TOO_SMALL, UNSUPPORTED_DEVICE, HIP_ERROR.
  */
@@ -166,14 +169,20 @@ FP8BS_API int fp8_block_gemm(const void *xq, const float *xs, const void *wq, co
  *     [0, M_total] are clamped by the kernel, so they cannot cause an
  *     out-of-bounds access (the result is then unspecified).
  *   y [M_total, N]: row r holds fp8_block_gemm of row r with its expert.
- * Workspace: fp8bs_grouped_workspace_size(E, M_total, N, K) bytes (0 today).
+ * Workspace: fp8bs_grouped_workspace_size(E, M_total, N, K) bytes, 16 per
+ *   row tile (at most ceil(M_total / 256) + E tiles): the call first writes
+ *   the table of (expert, first row, row count) of every row tile there from
+ *   group_offsets, on the device.  It need not be zeroed; calls that share a
+ *   workspace must not overlap in time.
  * Errors: as fp8_block_gemm; INVALID_ARG if E <= 0 with M_total > 0.
  */
 FP8BS_API int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                            const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
                            void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace sizes in bytes for the two GEMMs (pure functions of the shape; no device call). */
+/* Workspace sizes in bytes for the two GEMMs: functions of the shape (and of
+ * the FP8BS_GEMM_VARIANT / FP8BS_GEMM_KSPLIT measurement overrides, read once
+ * per process); no device call. */
 FP8BS_API size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 FP8BS_API size_t fp8bs_grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
 

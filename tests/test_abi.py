@@ -60,9 +60,16 @@ def test_workspace_queries_are_pure(fp8bs):
     L = fp8bs.lib()
     assert L.fp8bs_gemm_workspace_size(0, 128, 128) == 0
     assert L.fp8bs_gemm_workspace_size(-1, 128, 128) == 0
-    assert L.fp8bs_grouped_workspace_size(128, 65536, 1536, 2048) == 0
-    for M in (1, 16, 64, 256, 8192):
-        assert L.fp8bs_gemm_workspace_size(M, 28672, 4096) >= 0
+    # grouped: the row-tile table, 16 bytes per 256-row tile (at most ceil(M_total / 256) + E tiles)
+    assert L.fp8bs_grouped_workspace_size(128, 65536, 1536, 2048) == 16 * (65536 // 256 + 128)
+    assert L.fp8bs_grouped_workspace_size(0, 65536, 1536, 2048) == 0
+    # dense: fp32 partial sums (ksplit slices of M x N) when the product is split along K,
+    # never for products with at least one 256 x 256 tile per compute unit
+    assert L.fp8bs_gemm_workspace_size(8192, 28672, 4096) == 0
+    assert L.fp8bs_gemm_workspace_size(8192, 4096, 14336) == 0
+    for M, N, K in ((64, 4096, 14336), (256, 4096, 14336), (40, 512, 8192)):
+        ws = L.fp8bs_gemm_workspace_size(M, N, K)
+        assert ws > 0 and ws % (M * N * 4) == 0 and 2 <= ws // (M * N * 4) <= K // 128
 
 
 FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
@@ -112,11 +119,16 @@ def test_gemm_validation(fp8bs):
     assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, NULL, 0, NULL, 0, NULL) == 1   # null output
     assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, MISAL, 0, NULL, 0, NULL) == 1  # misaligned output
     assert g(NULL, NULL, FAKE, FAKE, 0, 128, 128, NULL, 0, NULL, 0, NULL) == 0   # M == 0
+    need = L.fp8bs_gemm_workspace_size(64, 4096, 14336)
+    assert g(FAKE, FAKE, FAKE, FAKE, 64, 4096, 14336, FAKE, 0, NULL, 0, NULL) == 4          # no workspace
+    assert g(FAKE, FAKE, FAKE, FAKE, 64, 4096, 14336, FAKE, 0, FAKE, need - 1, NULL) == 4   # too small
+    assert g(FAKE, FAKE, FAKE, FAKE, 64, 4096, 14336, FAKE, 0, MISAL, need, NULL) == 1      # misaligned
     gg = L.fp8_block_grouped_gemm
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1   # E == 0
     assert gg(FAKE, FAKE, FAKE, FAKE, NULL, 4, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1   # null offsets
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 128, FAKE, 0, NULL, 0, NULL) == 2    # N % 128
     assert gg(NULL, NULL, FAKE, FAKE, FAKE, 4, 0, 128, 128, NULL, 0, NULL, 0, NULL) == 0   # empty
+    assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 256, FAKE, 0, NULL, 0, NULL) == 4   # no table space
 
 
 def test_unsupported_device_without_gpu(fp8bs):

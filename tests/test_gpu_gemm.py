@@ -46,6 +46,9 @@ SMALL = [
     # X-row chunks at M = 256), 16 / 32 / 64-row W tiles, K blocks not a multiple of the 8 waves
     (1, 256, 1024), (5, 512, 2048), (16, 1024, 1152), (24, 16384, 1024), (33, 512, 1024), (64, 2048, 1280),
     (100, 384, 2048), (256, 128, 1024), (7, 8192, 1024),
+    # products split along K (fewer output tiles than compute units): 16 ranges of 4 blocks, uneven
+    # ranges of 4 and 5 blocks (K/128 = 23), and 256-row tiles with a ragged second row tile
+    (40, 512, 8192), (97, 512, 2944), (300, 512, 4096),
 ]
 
 
@@ -101,6 +104,8 @@ LARGE = [
     ("o_proj", 8192, 4096, 4096),
     ("decode1_gate_up", 1, 28672, 4096), ("decode16_down", 16, 4096, 14336),
     ("decode64_gate_up", 64, 28672, 4096), ("decode256_down", 256, 4096, 14336),
+    # one K block per tile and more tiles than workgroups: every workgroup walks several one-step tiles
+    ("k128_many_tiles", 4352, 4096, 128),
 ]
 
 
@@ -108,7 +113,7 @@ LARGE = [
 @pytest.mark.parametrize("case", LARGE, ids=lambda c: c[0])
 def test_gemm_parity_full_size_sampled(fp8bs, orc, case, mode):
     name, M, N, K = case
-    if mode == 1 and not name.startswith(("qkv", "decode1_")):
+    if mode == 1 and not name.startswith(("qkv", "decode1_", "k128")):
         pytest.skip("POW2 at full size is covered on qkv and decode")
     say("fp8_block_gemm %s M=%d N=%d K=%d mode=%d" % (name, M, N, K, mode))
     x, w, xd, wd, xq, xs, wq, ws, y32, y16, ((xq_r, xs_r), (wq_r, ws_r)) = _run_pair(fp8bs, orc, M, N, K, mode)
