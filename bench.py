@@ -53,7 +53,7 @@ COPY_BYTES = 1 << 30
 # Dominant kernel of each workload: (kernel-name prefix in a rocprofv3 trace,
 # source file, traffic record under profiles/).
 DOMINANT = {
-    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false>", GEMM_SRC,
+    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false>", GEMM_SRC,
               "gemm_dma_256x256_dense_m8192_traffic.json"),
     "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
 }
