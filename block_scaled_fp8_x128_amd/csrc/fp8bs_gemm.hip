@@ -86,7 +86,8 @@ struct GemmArgs {
     int tiles_n;            // N / BN
     int ksplit;             // persistent dense kernel: K ranges per output tile (1 = whole K)
     float *part;            // ksplit > 1: fp32 partial sums [ksplit][M][N]
-    const GroupTile *gtab;  // grouped, persistent kernel: the row tiles (tiles_m entries)
+    const GroupTile *gtab;  // grouped, persistent kernel: the row tiles (tiles_m entries) ...
+    const int32_t *gcount;  // ... of which the first *gcount exist
 };
 
 // Logical tile of workgroup `bid` (XCD-contiguous ranges, GROUP_M swizzle).
@@ -155,11 +156,13 @@ __device__ __forceinline__ bool expert_of_tile(const int32_t *offsets, int64_t E
 // The row tiles of the grouped form, written once per launch by one wave so
 // that the GEMM workgroups look a tile up with one scalar load: expert e
 // contributes ceil(count_e / BM) tiles, in expert order; entries past the
-// last tile get e = -1.  Offsets are clamped and made non-decreasing as in
-// expert_of_tile.  tiles_m >= ceil(M_total / BM) + E bounds the count.
+// last tile get e = -1, and *count receives the number of tiles, so that
+// the GEMM spreads exactly the existing tiles over the XCDs.  Offsets are
+// clamped and made non-decreasing as in expert_of_tile.  tiles_m >=
+// ceil(M_total / BM) + E bounds the count.
 template <int BM>
 __global__ __launch_bounds__(64) void grouped_tile_table_kernel(const int32_t *offsets, int64_t E, int64_t M_total,
-                                                                int tiles_m, GroupTile *tab)
+                                                                int tiles_m, GroupTile *tab, int32_t *count)
 {
     const int lane = threadIdx.x;
     int64_t prev_end = offsets[0];
@@ -196,6 +199,8 @@ __global__ __launch_bounds__(64) void grouped_tile_table_kernel(const int32_t *o
     }
     for (int t = base + lane; t < tiles_m; t += 64)
         tab[t] = GroupTile{0, -1, 0};
+    if (lane == 0)
+        *count = base < tiles_m ? base : tiles_m;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
@@ -458,8 +463,14 @@ struct TileGeo {
 template <int BM, int BN, bool GROUPED, bool SPLIT>
 __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, TileGeo &g)
 {
-    if (nunits % NUM_XCD == 0)
-        v = (v % NUM_XCD) * (nunits / NUM_XCD) + v / NUM_XCD;
+    {
+        // virtual ids v = x (mod 8) run on XCD x (the grid is a multiple of
+        // 8); give XCD x the contiguous unit range [x q + min(x, r), ...) of
+        // q or q + 1 units, a bijection for any unit count
+        const int x = v % NUM_XCD, i = v / NUM_XCD;
+        const int q = nunits / NUM_XCD, r = nunits % NUM_XCD;
+        v = x * q + (x < r ? x : r) + i;
+    }
     const int KB = (int)(a.K / BK);
     if (SPLIT) {
         const int ntl = a.tiles_m * a.tiles_n;
@@ -506,8 +517,11 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, T
 // (tile, K range) pairs and each writes its fp32 partial tile to the
 // partial-sum buffer (ksplit slices of M x N), summed by splitk_reduce_kernel.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs a)
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs args)
 {
+    GemmArgs a = args;
+    if constexpr (GROUPED)
+        a.tiles_m = *(const CONST_AS int32_t *)a.gcount; // the tiles that exist
     // three LDS stages (two steps of loads in flight) where they fit
     constexpr int NST = 3 * DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>::STAGE_BYTES <= 160 * 1024 ? 3 : 2;
     using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, NST>;
@@ -1289,6 +1303,9 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     }
 }
 
+// Grouped workspace: the tile count, padded to 16 bytes, then the tile table.
+constexpr size_t kGroupHeader = 16;
+
 // Row tiles of the grouped form's persistent kernels (the table's length):
 // BM = 256 unless forced to 128.
 static int64_t grouped_tiles_m(int64_t E, int64_t M_total)
@@ -1302,7 +1319,7 @@ size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K)
 {
     if (E <= 0 || M_total <= 0 || forced_variant() == V_SIMPLE || !dma_ok(N, K))
         return 0;
-    return (size_t)grouped_tiles_m(E, M_total) * sizeof(GroupTile);
+    return kGroupHeader + (size_t)grouped_tiles_m(E, M_total) * sizeof(GroupTile);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
@@ -1327,12 +1344,15 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
     if (grouped_workspace_size(E, M_total, N, K) > 0) {
         a.tiles_m = (int)grouped_tiles_m(E, M_total);
         a.tiles_n = (int)(N / 256);
-        a.gtab = (const GroupTile *)workspace;
+        int32_t *count = (int32_t *)workspace;
+        GroupTile *tab = (GroupTile *)((uint8_t *)workspace + kGroupHeader);
+        a.gtab = tab;
+        a.gcount = count;
         const bool big = fv != V_DMA;
         hipError_t e = big ? launch(grouped_tile_table_kernel<256>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
-                                    a.tiles_m, (GroupTile *)workspace)
+                                    a.tiles_m, tab, count)
                            : launch(grouped_tile_table_kernel<128>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
-                                    a.tiles_m, (GroupTile *)workspace);
+                                    a.tiles_m, tab, count);
         if (e != hipSuccess)
             return e;
         if (big)
