@@ -913,7 +913,9 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
     constexpr int NW = 8;
     constexpr int LPB = 2 * TN + 3 * TM; // loads per K block: W lo/hi, X lo/hi, X scale
     static_assert((D - 1) * LPB < 64, "outstanding loads must fit the vmcnt field");
-    __shared__ __attribute__((aligned(16))) float red[NW][TM * 16][TN * 16];
+    // (rows padded by 16 bytes: the 16 rows a 16-lane group writes then fall
+    // in different banks)
+    __shared__ __attribute__((aligned(16))) float red[NW][TM * 16][TN * 16 + 4];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1042,6 +1044,7 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
 //
 // Y = sum over the K ranges of the fp32 partial tiles, added in K-range order
 // (a fixed order, so results are deterministic), four columns per thread.
+// The loads of up to 8 ranges are issued before their sum.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, void *__restrict__ y,
                                                             int64_t MN, int ksplit)
@@ -1049,8 +1052,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     const int64_t n4 = MN / 4;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
         v4f v = *(const v4f *)(part + i * 4);
-        for (int s = 1; s < ksplit; ++s)
-            v += *(const v4f *)(part + s * MN + i * 4);
+        for (int s = 1; s < ksplit; s += 8) {
+            v4f t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s + u < ksplit)
+                    t[u] = *(const v4f *)(part + (s + u) * MN + i * 4);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s + u < ksplit)
+                    v += t[u];
+        }
         if (OUT_F32) {
             *(v4f *)((float *)y + i * 4) = v;
         } else {
