@@ -53,7 +53,7 @@ COPY_BYTES = 1 << 30
 # Dominant kernel of each workload: (kernel-name prefix in a rocprofv3 trace,
 # source file, traffic record under profiles/).
 DOMINANT = {
-    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false>", GEMM_SRC,
+    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false>", GEMM_SRC,
               "gemm_dma_256x256_dense_m8192_traffic.json"),
     "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
 }
@@ -147,6 +147,9 @@ def traffic_for(workload):
 # ---------------------------------------------------------------------------
 
 def dense_workload(fp8bs, dev, mode):
+    # POW2 scales go to the entry points that apply them through the matrix cores
+    gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
+    grouped = fp8bs.fp8_block_grouped_gemm_pow2 if mode else fp8bs.fp8_block_grouped_gemm
     import synth
     import torch
     M = 8192
@@ -168,7 +171,7 @@ def dense_workload(fp8bs, dev, mode):
         for b in bufs:
             maybe(timer, "quant_act_" + b["name"], lambda: fp8bs.quant_act_1x128(b["x"], mode, out=(b["xq"], b["xs"])))
             maybe(timer, "gemm_" + b["name"],
-                  lambda: fp8bs.fp8_block_gemm(b["xq"], b["xs"], b["wq"], b["ws"], out=b["y"]))
+                  lambda: gemm(b["xq"], b["xs"], b["wq"], b["ws"], out=b["y"]))
 
     flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
     return step, bufs, flops
@@ -267,6 +270,9 @@ def cpu_baseline_recal(target_s=12.0):
 
 
 def decode_workload(fp8bs, dev, mode):
+    # POW2 scales go to the entry points that apply them through the matrix cores
+    gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
+    grouped = fp8bs.fp8_block_grouped_gemm_pow2 if mode else fp8bs.fp8_block_grouped_gemm
     import synth
     import torch
     pairs = []
@@ -295,7 +301,7 @@ def decode_workload(fp8bs, dev, mode):
             wq, ws = p["copies"][c]
             maybe(timer, "quant_" + p["name"], lambda p=p: fp8bs.quant_act_1x128(p["x"], mode, out=(p["xq"], p["xs"])))
             maybe(timer, "gemm_" + p["name"],
-                  lambda p=p, wq=wq, ws=ws: fp8bs.fp8_block_gemm(p["xq"], p["xs"], wq, ws, out=p["y"],
+                  lambda p=p, wq=wq, ws=ws: gemm(p["xq"], p["xs"], wq, ws, out=p["y"],
                                                                  workspace=p["ws_buf"]))
 
     flops = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pairs)
@@ -303,6 +309,9 @@ def decode_workload(fp8bs, dev, mode):
 
 
 def moe_workload(fp8bs, dev, mode):
+    # POW2 scales go to the entry points that apply them through the matrix cores
+    gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
+    grouped = fp8bs.fp8_block_grouped_gemm_pow2 if mode else fp8bs.fp8_block_grouped_gemm
     import synth
     import torch
     E, H, F, T, TOPK = 128, 2048, 768, 8192, 8
@@ -334,11 +343,11 @@ def moe_workload(fp8bs, dev, mode):
                                                                                outs=[(b["w1q"], b["w1s"]),
                                                                                      (b["w2q"], b["w2s"])]))
         maybe(timer, "quant_act_gate_up", lambda: fp8bs.quant_act_1x128(x1, mode, out=(b["x1q"], b["x1s"])))
-        maybe(timer, "grouped_gate_up", lambda: fp8bs.fp8_block_grouped_gemm(
+        maybe(timer, "grouped_gate_up", lambda: grouped(
             b["x1q"], b["x1s"], b["w1q"].view(E, 2 * F, H), b["w1s"].view(E, 2 * F // 128, H // 128), offs_d,
             out=b["y1"], workspace=b["wk1"]))
         maybe(timer, "quant_act_down", lambda: fp8bs.quant_act_1x128(x2, mode, out=(b["x2q"], b["x2s"])))
-        maybe(timer, "grouped_down", lambda: fp8bs.fp8_block_grouped_gemm(
+        maybe(timer, "grouped_down", lambda: grouped(
             b["x2q"], b["x2s"], b["w2q"].view(E, H, F), b["w2s"].view(E, H // 128, F // 128), offs_d, out=b["y2"],
             workspace=b["wk2"]))
 

@@ -37,6 +37,8 @@ EXPORTS = (
     "quant_w_128x128_batched",
     "fp8_block_gemm",
     "fp8_block_grouped_gemm",
+    "fp8_block_gemm_pow2",
+    "fp8_block_grouped_gemm_pow2",
     "fp8bs_gemm_workspace_size",
     "fp8bs_grouped_workspace_size",
     "fp8bs_status_string",
@@ -65,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
         L.fp8_block_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P, SZ, P]
+        L.fp8_block_gemm_pow2.argtypes = L.fp8_block_gemm.argtypes
+        L.fp8_block_grouped_gemm_pow2.argtypes = L.fp8_block_grouped_gemm.argtypes
         L.fp8bs_gemm_workspace_size.argtypes = [I64, I64, I64]
         L.fp8bs_gemm_workspace_size.restype = SZ
         L.fp8bs_grouped_workspace_size.argtypes = [I64, I64, I64, I64]
@@ -73,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
         for fn in ("quant_act_1x128", "quant_w_128x128", "quant_w_128x128_batched", "fp8_block_gemm",
-                   "fp8_block_grouped_gemm"):
+                   "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2"):
             getattr(L, fn).restype = I32
         _lib = L
     return _lib
@@ -200,6 +204,15 @@ def grouped_workspace_size(E: int, M_total: int, N: int, K: int) -> int:
 
 def fp8_block_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, workspace=None):
     """Y [M, N] = dequant(xq, xs) @ dequant(wq, ws)^T."""
+    return _gemm("fp8_block_gemm", xq, xs, wq, ws, out_dtype, out, workspace)
+
+
+def fp8_block_gemm_pow2(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """fp8_block_gemm for power-of-2 scales (POW2-quantized operands): the scales go to the matrix cores."""
+    return _gemm("fp8_block_gemm_pow2", xq, xs, wq, ws, out_dtype, out, workspace)
+
+
+def _gemm(fn, xq, xs, wq, ws, out_dtype, out, workspace):
     xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
     xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
     M, K = xq.shape
@@ -213,14 +226,23 @@ def fp8_block_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, workspace
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().fp8_block_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code,
-                              _ptr(workspace), wsz, _stream(xq))
-    _check("fp8_block_gemm", st)
+    st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code,
+                            _ptr(workspace), wsz, _stream(xq))
+    _check(fn, st)
     return out
 
 
 def fp8_block_grouped_gemm(xq, xs, wq, ws, group_offsets, out_dtype=torch.bfloat16, out=None, workspace=None):
     """Y [M_total, N]: rows offs[e]..offs[e+1]-1 multiplied by expert e's weights."""
+    return _grouped("fp8_block_grouped_gemm", xq, xs, wq, ws, group_offsets, out_dtype, out, workspace)
+
+
+def fp8_block_grouped_gemm_pow2(xq, xs, wq, ws, group_offsets, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """fp8_block_grouped_gemm for power-of-2 scales (POW2-quantized operands)."""
+    return _grouped("fp8_block_grouped_gemm_pow2", xq, xs, wq, ws, group_offsets, out_dtype, out, workspace)
+
+
+def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace):
     xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
     xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
     if group_offsets.dtype != torch.int32 or not group_offsets.is_cuda:
@@ -236,7 +258,7 @@ def fp8_block_grouped_gemm(xq, xs, wq, ws, group_offsets, out_dtype=torch.bfloat
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().fp8_block_grouped_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(group_offsets), E, M, N, K,
-                                      _ptr(out), code, _ptr(workspace), wsz, _stream(xq))
-    _check("fp8_block_grouped_gemm", st)
+    st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(group_offsets), E, M, N, K,
+                            _ptr(out), code, _ptr(workspace), wsz, _stream(xq))
+    _check(fn, st)
     return out

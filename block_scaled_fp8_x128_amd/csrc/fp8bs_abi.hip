@@ -181,8 +181,9 @@ size_t fp8bs_grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64
     return fp8bs::grouped_workspace_size(E, M_total, N, K);
 }
 
-int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
-                   void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+static int gemm_impl(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                     int64_t K, void *y, int out_dtype, int pow2, void *workspace, size_t workspace_bytes,
+                     void *stream)
 {
     int st = check_gemm_common(xq, xs, y, M, N, K, out_dtype);
     if (st != FP8BS_OK)
@@ -198,13 +199,13 @@ int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float 
         return FP8BS_INVALID_ARG;
     if ((st = check_device()) != FP8BS_OK)
         return st;
-    return status_of(fp8bs::launch_gemm(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, workspace,
+    return status_of(fp8bs::launch_gemm(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, pow2, workspace,
                                         (hipStream_t)stream));
 }
 
-int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
-                           const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
-                           int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+static int grouped_impl(const void *xq, const float *xs, const void *wq, const float *ws,
+                        const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
+                        int out_dtype, int pow2, void *workspace, size_t workspace_bytes, void *stream)
 {
     int st = check_gemm_common(xq, xs, y, M_total, N, K, out_dtype);
     if (st != FP8BS_OK)
@@ -226,7 +227,35 @@ int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, cons
     if ((st = check_device()) != FP8BS_OK)
         return st;
     return status_of(fp8bs::launch_grouped_gemm(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y,
-                                                out_dtype == FP8BS_OUT_FP32, workspace, (hipStream_t)stream));
+                                                out_dtype == FP8BS_OUT_FP32, pow2, workspace, (hipStream_t)stream));
+}
+
+int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+                   void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_impl(xq, xs, wq, ws, M, N, K, y, out_dtype, 0, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_gemm_pow2(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                        int64_t K, void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_impl(xq, xs, wq, ws, M, N, K, y, out_dtype, 1, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                           const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
+                           int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return grouped_impl(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y, out_dtype, 0, workspace, workspace_bytes,
+                        stream);
+}
+
+int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const void *wq, const float *ws,
+                                const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return grouped_impl(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y, out_dtype, 1, workspace, workspace_bytes,
+                        stream);
 }
 
 } // extern "C"

@@ -516,7 +516,11 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, T
 // whose out-of-range rows the hardware drops.  SPLIT: the work units are
 // (tile, K range) pairs and each writes its fp32 partial tile to the
 // partial-sum buffer (ksplit slices of M x N), summed by splitk_reduce_kernel.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT>
+// POW2: every scale is a power of two (the power-of-2 scale option of the
+// article's closing section), so each K block's scale product 2^e is exact
+// and goes to the MFMA's E8M0 scale operand: the matrix core accumulates
+// 2^e * P into the accumulator itself and the fp32 VALU rescale disappears.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT, bool POW2>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs args)
 {
     GemmArgs a = args;
@@ -698,6 +702,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         const uint8_t *Ln = lds + nstage * C::STAGE_BYTES;
         v4f part[2];
         float xs_next[C::TM];
+        // POW2: the E8M0 code of each row tile's scale product (its biased
+        // exponent; the product of two powers of two is exact in fp32).  Lane
+        // l's scale applies to the activation row l % 16 whose fragment it
+        // holds, which is the row its scale product belongs to.
+        int e8[C::TM];
+        if constexpr (POW2) {
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+                e8[i] = (int)(__builtin_bit_cast(uint32_t, sc[i]) >> 23);
+        }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
             const bool last = j + 1 == C::TN;
@@ -729,14 +743,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 const int t = j * C::TM + i;
-                part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                               0, 0, 0, 127, 0, 127);
+                if constexpr (POW2)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], acc[i][j], 0, 0, 0, 127, 0,
+                                                                                 e8[i]);
+                else
+                    part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        aw, bx[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
                 // issue order, fenced: each MFMA, then the rescale of the
                 // previous one (whose product has had a full MFMA to land),
                 // and in the last group the next step's X fragment it freed;
                 // after the barrier, the next loads one or two per MFMA
                 __builtin_amdgcn_sched_barrier(0);
-                if (t > 0)
+                if (!POW2 && t > 0)
                     rescale(t - 1, part[(t - 1) & 1]);
                 if (last)
                     bx[i] = frag(Ln + xo[0] + i * 2048, Ln + xo[1] + i * 2048);
@@ -750,7 +768,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        rescale(C::TM * C::TN - 1, part[(C::TM * C::TN - 1) & 1]);
+        if constexpr (!POW2)
+            rescale(C::TM * C::TN - 1, part[(C::TM * C::TN - 1) & 1]);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
             sc[i] = xs_next[i] * sw_next;
@@ -1128,21 +1147,22 @@ static hipError_t run_simple(GemmArgs a, int grid, bool out_f32, hipStream_t str
 // the 8 XCDs so that the XCD-contiguous unit ranges line up with the dispatch.
 constexpr int kPersistentGrid = 256;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED>
-static hipError_t run_dma(GemmArgs a, bool out_f32, hipStream_t stream)
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED, bool POW2>
+static hipError_t run_dma_t(GemmArgs a, bool out_f32, hipStream_t stream)
 {
     const dim3 block(WAVES_M * WAVES_N * 64);
     const int units = a.tiles_m * a.tiles_n * a.ksplit;
     const int grid = units < kPersistentGrid ? units : kPersistentGrid;
     if (GROUPED || a.ksplit == 1) {
         if (out_f32)
-            return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED, false>, dim3(grid), block, 0, stream,
-                          a);
-        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED, false>, dim3(grid), block, 0, stream, a);
+            return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED, false, POW2>, dim3(grid), block, 0,
+                          stream, a);
+        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED, false, POW2>, dim3(grid), block, 0,
+                      stream, a);
     }
     if constexpr (!GROUPED) { // (the grouped form is never split)
-        const hipError_t e =
-            launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, true>, dim3(grid), block, 0, stream, a);
+        const hipError_t e = launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, true, POW2>, dim3(grid),
+                                    block, 0, stream, a);
         if (e != hipSuccess)
             return e;
         const int64_t MN = a.M * a.N;
@@ -1155,6 +1175,14 @@ static hipError_t run_dma(GemmArgs a, bool out_f32, hipStream_t stream)
                       MN, a.ksplit);
     }
     return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED>
+static hipError_t run_dma(GemmArgs a, bool out_f32, bool pow2, hipStream_t stream)
+{
+    if (pow2)
+        return run_dma_t<BM, BN, WAVES_M, WAVES_N, GROUPED, true>(a, out_f32, stream);
+    return run_dma_t<BM, BN, WAVES_M, WAVES_N, GROUPED, false>(a, out_f32, stream);
 }
 
 // The large-tile kernels: N a multiple of their 256-wide tile, 32-bit
@@ -1285,7 +1313,7 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K)
 }
 
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
-                       int64_t K, void *y, int out_fp32, void *workspace, hipStream_t stream)
+                       int64_t K, void *y, int out_fp32, int pow2, void *workspace, hipStream_t stream)
 {
     if (M == 0)
         return hipSuccess;
@@ -1307,9 +1335,9 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     case K_SKINNY:
         return run_skinny(a, out_fp32 != 0, stream);
     case K_DMA256:
-        return run_dma<256, 256, 4, 2, false>(a, out_fp32 != 0, stream);
+        return run_dma<256, 256, 4, 2, false>(a, out_fp32 != 0, pow2 != 0, stream);
     case K_DMA128:
-        return run_dma<128, 256, 2, 4, false>(a, out_fp32 != 0, stream);
+        return run_dma<128, 256, 2, 4, false>(a, out_fp32 != 0, pow2 != 0, stream);
     default:
         return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
     }
@@ -1336,7 +1364,7 @@ size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K)
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
-                               int out_fp32, void *workspace, hipStream_t stream)
+                               int out_fp32, int pow2, void *workspace, hipStream_t stream)
 {
     if (M_total == 0)
         return hipSuccess;
@@ -1368,8 +1396,8 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
         if (e != hipSuccess)
             return e;
         if (big)
-            return run_dma<256, 256, 4, 2, true>(a, out_fp32 != 0, stream);
-        return run_dma<128, 256, 2, 4, true>(a, out_fp32 != 0, stream);
+            return run_dma<256, 256, 4, 2, true>(a, out_fp32 != 0, pow2 != 0, stream);
+        return run_dma<128, 256, 2, 4, true>(a, out_fp32 != 0, pow2 != 0, stream);
     }
     a.tiles_m = (int)((M_total + 127) / 128 + E);
     a.tiles_n = (int)(N / 128);

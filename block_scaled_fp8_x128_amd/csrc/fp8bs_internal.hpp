@@ -45,11 +45,13 @@ hipError_t launch_quant_w(const WTensor *t, int64_t count, int mode, hipStream_t
 // ---- GEMMs (fp8bs_gemm.hip) --------------------------------------------------
 
 size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+// pow2: every scale is a power of two (the kernels then apply the scales
+// through the matrix cores' E8M0 operands where they can)
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
-                       int64_t K, void *y, int out_fp32, void *workspace, hipStream_t stream);
+                       int64_t K, void *y, int out_fp32, int pow2, void *workspace, hipStream_t stream);
 size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
-                               int out_fp32, void *workspace, hipStream_t stream);
+                               int out_fp32, int pow2, void *workspace, hipStream_t stream);
 
 } // namespace fp8bs

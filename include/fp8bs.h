@@ -181,6 +181,33 @@ FP8BS_API int fp8_block_grouped_gemm(const void *xq, const float *xs, const void
                            const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
                            void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * fp8_block_gemm_pow2, fp8_block_grouped_gemm_pow2 -- the two GEMMs for
+ * operands quantized with power-of-2 scales (the power-of-2 scaling option in
+ * the article's closing section; scale_mode FP8BS_SCALE_POW2 of the
+ * quantizers).  Arguments, layouts, workspace and errors are exactly those of
+ * fp8_block_gemm and fp8_block_grouped_gemm.
+ *
+ * Precondition: every xs and ws entry is a power of two, and every product
+ * xs[m, kb] * ws[n/128, kb] is a normal fp32 number (>= 2^-126), which holds
+ * for POW2-quantized data of any ordinary magnitude.  Each K block's scale
+ * product 2^e is then exact, and on the large-tile kernels it is handed to
+ * the matrix cores' E8M0 block-scale operand: the MFMA accumulates 2^e * P
+ * directly, with no fp32 rescale pass.  Only the exponent of each scale
+ * product is used there; with scales that break the precondition the result
+ * is unspecified (it is never a memory fault).  Results agree with
+ * fp8_block_gemm on the same operands to within fp32 rounding of the
+ * accumulation order; the bf16 output is again the round-to-nearest-even of
+ * the fp32 output of the same call shape.
+ */
+FP8BS_API int fp8_block_gemm_pow2(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M,
+                                  int64_t N, int64_t K, void *y, int out_dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+FP8BS_API int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const void *wq, const float *ws,
+                                          const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N,
+                                          int64_t K, void *y, int out_dtype, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Workspace sizes in bytes for the two GEMMs: functions of the shape (and of
  * the FP8BS_GEMM_VARIANT / FP8BS_GEMM_KSPLIT measurement overrides, read once
  * per process); no device call. */

@@ -27,6 +27,16 @@ def fp8bs():
     return m
 
 
+def _pow2_outputs(fn, *args):
+    """fp32 and bf16 outputs of a _pow2 entry point (the matrix cores apply the scales)."""
+    y32 = fn(*args, out_dtype=torch.float32)
+    y16 = fn(*args, out_dtype=torch.bfloat16)
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    y32b = fn(*args, out_dtype=torch.float32)
+    assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32))
+    return y32
+
+
 def _run_pair(fp8bs, orc, M, N, K, mode, seed_sub=0):
     x = synth.activations(M, K, seed=synth.SEED, sub=synth.SUB_X + 10 * seed_sub)
     w = synth.weights(N, K, seed=synth.SEED, sub=synth.SUB_W + 10 * seed_sub)
@@ -67,6 +77,9 @@ def test_gemm_parity_full_output(fp8bs, orc, shape, mode):
     # deterministic: a second run is bit-identical
     y32b = fp8bs.fp8_block_gemm(xq, xs, wq, ws, out_dtype=torch.float32)
     assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32))
+    if mode == 1:
+        # power-of-2 scales: the entry point that hands them to the matrix cores
+        gemm_gate("Y fp32 (pow2 entry)", host(_pow2_outputs(fp8bs.fp8_block_gemm_pow2, xq, xs, wq, ws)), ref)
     # reported, not gated: error against the unquantized bf16 product
     yb = (xd.float() @ wd.float().T)
     say("  vs unquantized bf16 GEMM: max|err|/rms = %.3e" %
@@ -87,6 +100,14 @@ def test_gemm_integer_special_case(fp8bs):
     y = fp8bs.fp8_block_gemm(to_dev(xq), to_dev(np.ones((M, K // 128), np.float32)), to_dev(wq),
                              to_dev(np.ones((N // 128, K // 128), np.float32)), out_dtype=torch.float32)
     assert np.array_equal(host(y), ref)
+    # unit scales are powers of two: the scaled-MFMA path is exact here too, and so are other
+    # power-of-2 scales (2^-3 on X, 2^5 on W multiply the exact integer result by 4)
+    y = fp8bs.fp8_block_gemm_pow2(to_dev(xq), to_dev(np.ones((M, K // 128), np.float32)), to_dev(wq),
+                                  to_dev(np.ones((N // 128, K // 128), np.float32)), out_dtype=torch.float32)
+    assert np.array_equal(host(y), ref)
+    y = fp8bs.fp8_block_gemm_pow2(to_dev(xq), to_dev(np.full((M, K // 128), 0.125, np.float32)), to_dev(wq),
+                                  to_dev(np.full((N // 128, K // 128), 32.0, np.float32)), out_dtype=torch.float32)
+    assert np.array_equal(host(y), 4 * ref)
 
 
 def test_gemm_empty(fp8bs):
@@ -126,6 +147,9 @@ def test_gemm_parity_full_size_sampled(fp8bs, orc, case, mode):
     y = host(y32)[rows, cols]
     gemm_gate("Y fp32 (sampled %d)" % rows.size, y, ref)
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    if mode == 1:
+        yp = host(_pow2_outputs(fp8bs.fp8_block_gemm_pow2, xq, xs, wq, ws))[rows, cols]
+        gemm_gate("Y fp32 (pow2 entry, sampled %d)" % rows.size, yp, ref)
 
 
 # ---- grouped (MoE) ---------------------------------------------------------------
@@ -147,6 +171,8 @@ def _grouped(fp8bs, orc, counts, N, K, mode, token_rows=None, x_tok=None, seed_s
     offs_d = to_dev(offs)
     y32 = fp8bs.fp8_block_grouped_gemm(xq, xs, wq, ws, offs_d, out_dtype=torch.float32)
     y16 = fp8bs.fp8_block_grouped_gemm(xq, xs, wq, ws, offs_d, out_dtype=torch.bfloat16)
+    if mode == 1:  # power-of-2 scales: the scaled-MFMA entry point, gated by the callers like y32
+        y32 = (y32, _pow2_outputs(fp8bs.fp8_block_grouped_gemm_pow2, xq, xs, wq, ws, offs_d))
     xq_r, xs_r = orc.quant_act_1x128(x, mode)
     wq_r, ws_r = orc.quant_w_128x128(w.reshape(E * N, K), mode)
     wq_r = wq_r.reshape(E, N, K)
@@ -171,6 +197,9 @@ def test_grouped_parity(fp8bs, orc, counts, mode):
     say("fp8_block_grouped_gemm counts=%s mode=%d" % (counts[:8], mode))
     xq_r, xs_r, wq_r, ws_r, offs, y32, y16 = _grouped(fp8bs, orc, counts, N, K, mode, seed_sub=len(counts))
     ref = orc.grouped_gemm(xq_r, xs_r, wq_r, ws_r, offs)
+    if mode == 1:
+        y32, yp = y32
+        gemm_gate("Y fp32 (pow2 entry)", host(yp), ref)
     gemm_gate("Y fp32", host(y32), ref)
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
 
@@ -194,5 +223,8 @@ def test_grouped_parity_moe_full_size_sampled(fp8bs, orc, proj, mode):
     xq_r, xs_r, wq_r, ws_r, offs, y32, y16 = _grouped(fp8bs, orc, counts, N, K, mode, **args)
     rows, cols = sample_positions(int(offs[-1]), N, 4000, seed=N)
     ref = orc.grouped_gemm_sampled(xq_r, xs_r, wq_r, ws_r, offs, rows, cols)
+    if mode == 1:
+        y32, yp = y32
+        gemm_gate("Y fp32 (pow2 entry, sampled %d)" % rows.size, host(yp)[rows, cols], ref)
     gemm_gate("Y fp32 (sampled %d)" % rows.size, host(y32)[rows, cols], ref)
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
