@@ -926,11 +926,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 // through the buffer range check, and their scales as zeros.  At the end the
 // 8 per-wave partial tiles are summed through LDS in wave order (a fixed
 // order, so results are deterministic) and written out.
+constexpr int kSkinnyMaxIt = 16; // K blocks per wave of the weight-streaming kernel (K <= 16384)
+
 template <int TM, int TN, int D, bool OUT_F32>
 __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int NW = 8;
-    constexpr int LPB = 2 * TN + 3 * TM; // loads per K block: W lo/hi, X lo/hi, X scale
+    constexpr int LPB = 2 * TN + 3 * TM + 1; // loads per K block: W lo/hi, X lo/hi, X scale, W scale
     static_assert((D - 1) * LPB < 64, "outstanding loads must fit the vmcnt field");
     // (rows padded by 16 bytes: the 16 rows a 16-lane group writes then fall
     // in different banks)
@@ -951,21 +953,26 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.xq + m0 * K, mrows * K);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.xs + m0 * KB, mrows * KB * 4);
     const __amdgpu_buffer_rsrc_t none = make_rsrc(a.xq, 0);
+    // the weight scales of this tile's 128-row block, loaded with the operands
+    // (one uniform dword per K block) so that no scalar-load wait sits among
+    // the MFMAs
+    const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws + (n0 / 128) * KB, KB * 4);
     const int loff = (int)(fr * K + fg * 32);
     const int soff = (int)(fr * KB * 4);
-    const CONST_AS float *ws_row = (const CONST_AS float *)(a.ws + (n0 / 128) * KB);
 
     const int nk = wave < KB ? (int)((KB - wave + NW - 1) / NW) : 0; // this wave's K blocks
 
     v8i wf[D][TN], xf[D][TM];
-    float xv[D][TM];
+    float xv[D][TM], wv[D];
     // Loads of this wave's it-th K block into ring slot `slot`.  Blocks past
     // the end issue the same instructions on an empty range (no traffic), so
     // every step issues LPB loads and the waits below are fixed counts.
     auto load = [&](int slot, int it) {
         const bool live = it < nk;
         const int kb = live ? (int)(wave + (int64_t)it * NW) : 0;
-        const __amdgpu_buffer_rsrc_t w_ = live ? wr : none, x_ = live ? xr : none, s_ = live ? sr : none;
+        const __amdgpu_buffer_rsrc_t w_ = live ? wr : none, x_ = live ? xr : none, s_ = live ? sr : none,
+                                     t_ = live ? wsr : none;
+        wv[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t_, 0, kb * 4, 0));
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int so = kb * BK + (int)(j * 16 * K);
@@ -993,39 +1000,40 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
         for (int j = 0; j < TN; ++j)
             acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // The K loop is unrolled completely (a wave has at most kSkinnyMaxIt
+    // blocks; the launcher guarantees it), so the compiler sees which loads
+    // are in flight at every wait: a rolled loop made it drain all of them
+    // at the loop head.
 #pragma unroll
     for (int d = 0; d < D; ++d)
         load(d, d);
-    for (int base = 0; base < nk; base += D) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int it = base + d;
-            wait_vmcnt<(D - 1) * LPB>(); // block `it` landed; D - 1 younger blocks may fly
-            if (it < nk) {
-                const float sw = ws_row[wave + (int64_t)it * NW];
-                float sc[TM];
+    for (int it = 0; it < kSkinnyMaxIt; ++it) {
+        const int d = it % D;
+        wait_vmcnt<(D - 1) * LPB>(); // block `it` landed; D - 1 younger blocks may fly
+        const float sw = wv[d];
+        float sc[TM];
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    sc[i] = xv[d][i] * sw;
-                v4f part[2];
+        for (int i = 0; i < TM; ++i)
+            sc[i] = xv[d][i] * sw;
+        v4f part[2];
 #pragma unroll
-                for (int t = 0; t < TM * TN; ++t) {
-                    const int i = t % TM, j = t / TM;
-                    part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[d][j], xf[d][i],
-                                                                                   v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                                   0, 127, 0, 127);
-                    if (t > 0) {
-                        const int pi = (t - 1) % TM, pj = (t - 1) / TM;
-                        acc[pi][pj] = __builtin_elementwise_fma(v4f{sc[pi], sc[pi], sc[pi], sc[pi]},
-                                                                part[(t - 1) & 1], acc[pi][pj]);
-                    }
-                }
-                constexpr int T = TM * TN;
-                acc[TM - 1][TN - 1] = __builtin_elementwise_fma(v4f{sc[TM - 1], sc[TM - 1], sc[TM - 1], sc[TM - 1]},
-                                                                part[(T - 1) & 1], acc[TM - 1][TN - 1]);
+        for (int t = 0; t < TM * TN; ++t) {
+            const int i = t % TM, j = t / TM;
+            part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[d][j], xf[d][i], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 127, 0, 127);
+            if (t > 0) {
+                const int pi = (t - 1) % TM, pj = (t - 1) / TM;
+                acc[pi][pj] = __builtin_elementwise_fma(v4f{sc[pi], sc[pi], sc[pi], sc[pi]}, part[(t - 1) & 1],
+                                                        acc[pi][pj]);
             }
-            load(d, it + D);
         }
+        constexpr int T = TM * TN;
+        acc[TM - 1][TN - 1] = __builtin_elementwise_fma(v4f{sc[TM - 1], sc[TM - 1], sc[TM - 1], sc[TM - 1]},
+                                                        part[(T - 1) & 1], acc[TM - 1][TN - 1]);
+        if (it + 1 >= nk)
+            break; // (uniform over the wave; later blocks are past this wave's share)
+        load(d, it + D);
     }
     wait_vmcnt<0>();
 
@@ -1195,10 +1203,11 @@ static bool dma_ok(int64_t N, int64_t K)
 
 // The weight-streaming kernel: at most 256 activation rows, N a multiple of
 // 16, 32-bit buffer offsets (16 rows of K bytes per tile group, 128 rows of
-// X), and enough K blocks for the waves to share.
+// X), enough K blocks for the waves to share, and at most kSkinnyMaxIt of
+// them per wave.
 static bool skinny_ok(int64_t M, int64_t N, int64_t K)
 {
-    return M <= 256 && N % 16 == 0 && 128 * K < ((int64_t)1 << 31) && K / 128 >= 8;
+    return M <= 256 && N % 16 == 0 && 128 * K < ((int64_t)1 << 31) && K / 128 >= 8 && K / 128 <= 8 * kSkinnyMaxIt;
 }
 
 // Rows up to which the weight-streaming kernel is the automatic choice (above
