@@ -72,6 +72,9 @@ int check_gemm_common(const void *xq, const float *xs, const void *y, int64_t M,
         return FP8BS_UNSUPPORTED_SHAPE;
     if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
         return FP8BS_UNSUPPORTED_SHAPE;
+    // output tiles are counted in 32-bit integers (work units, grid sizes)
+    if (((M + 127) / 128) * (N / 128) >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
     if (!tensor_ok(xq, M * K, 16) || !tensor_ok(xs, M * K, 4) || !tensor_ok(y, M * N, 16))
         return FP8BS_INVALID_ARG;
     return FP8BS_OK;

@@ -148,7 +148,8 @@ FP8BS_API int quant_w_128x128_batched(int64_t count, const void *const *w_bf16, 
  *   as fp8bs_gemm_workspace_size(M, N, K) returns (0 for the other shapes,
  *   where workspace may be NULL).  It need not be zeroed; its contents are
  *   overwritten.  Two calls that share a workspace must not overlap in time.
- * Errors: INVALID_ARG, UNSUPPORTED_SHAPE (N or K not a multiple of 128),
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE (N or K not a multiple of 128, or
+ *   ceil(M / 128) * N / 128 of 2^31 or more output tiles),
  * WORKSPACE_TOO_SMALL, UNSUPPORTED_DEVICE, HIP_ERROR.
  */
 FP8BS_API int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,

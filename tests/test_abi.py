@@ -119,6 +119,7 @@ def test_gemm_validation(fp8bs):
     assert g(FAKE, FAKE, NULL, FAKE, 8, 128, 128, FAKE, 0, NULL, 0, NULL) == 1   # null weights
     assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, NULL, 0, NULL, 0, NULL) == 1   # null output
     assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, MISAL, 0, NULL, 0, NULL) == 1  # misaligned output
+    assert g(FAKE, FAKE, FAKE, FAKE, 2**30, 2**30, 128, FAKE, 0, NULL, 0, NULL) == 2  # 2^36 output tiles
     assert g(NULL, NULL, FAKE, FAKE, 0, 128, 128, NULL, 0, NULL, 0, NULL) == 0   # M == 0
     need = L.fp8bs_gemm_workspace_size(64, 4096, 14336)
     assert g(FAKE, FAKE, FAKE, FAKE, 64, 4096, 14336, FAKE, 0, NULL, 0, NULL) == 4          # no workspace
