@@ -76,7 +76,11 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, const BlockQuant<MODE> &bq
 // 16-lane DPP row of a wave owns one block per step (16 lanes x 16 bytes);
 // a wave's four rows cover 4 consecutive blocks, i.e. 1 KiB of contiguous
 // bf16 per load instruction, and each lane keeps QA_UNROLL loads in flight.
-constexpr int QA_UNROLL = 4;
+// Two (8 blocks per wave) measured best on gfx950: against four and eight,
+// more, shorter waves fill the chip sooner at the sizes of a layer's
+// activations (8192 x 4096: 19.5 us against 21.1 with four); one load per lane
+// leaves too little in flight on the large shapes.
+constexpr int QA_UNROLL = 2;
 constexpr int QA_THREADS = 256;
 constexpr int QA_BLOCKS_PER_WG = (QA_THREADS / 64) * 4 * QA_UNROLL;
 
