@@ -375,7 +375,9 @@ def _pmc_means(db, counter):
     return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
 
 
-def summarize_pmc(fetch_db, write_db, workload, command):
+def summarize_pmc(fetch_db, write_db, workload, command, out=None):
+    """Write the traffic record of `workload`'s dominant kernel (to profiles/
+    unless `out` names another file) and return it."""
     kprefix, src, fname = DOMINANT[workload]
     fetch = _pmc_means(fetch_db, "FETCH_SIZE")
     write = _pmc_means(write_db, "WRITE_SIZE")
@@ -403,11 +405,12 @@ def summarize_pmc(fetch_db, write_db, workload, command):
            "hbm_fetch_bytes_per_launch": kf * 1024.0 * f_scale,
            "hbm_write_bytes_per_launch": kw * 1024.0 * w_scale}
     rec["hbm_bytes_per_launch"] = rec["hbm_fetch_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
-    out = os.path.join(ROOT, "profiles", fname)
+    out = out or os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+    return rec
 
 
 # ---------------------------------------------------------------------------

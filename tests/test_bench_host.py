@@ -1,0 +1,83 @@
+"""Host logic of bench.py (no GPU): the one-GPU contract and the rocprofv3
+counter records that give the roofline its HBM traffic."""
+
+import importlib.util
+import json
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _counter_db(path, counter, rows):
+    """A database shaped like rocprofv3's: one row per (dispatch, counter instance)."""
+    c = sqlite3.connect(path)
+    c.execute("create table counters_collection (kernel_name text, counter_name text, value real, "
+              "duration integer, dispatch_id integer)")
+    c.executemany("insert into counters_collection values (?, ?, ?, 0, ?)",
+                  [(k, counter, v, d) for k, v, d in rows])
+    c.commit()
+    c.close()
+
+
+def test_traffic_record_scales_by_the_copy_calibration(bench, tmp_path):
+    kname = "void " + bench.DOMINANT["dense"][0] + "(fp8bs::GemmArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    gib_kib = bench.COPY_BYTES / 1024
+    # the copy's 1 GiB reads as half in FETCH_SIZE and in full in WRITE_SIZE; counter values of one
+    # dispatch are split over two instances (summed), and two dispatches are averaged
+    _counter_db(tmp_path / "f.db", "FETCH_SIZE",
+                [(copy, gib_kib / 4, 1), (copy, gib_kib / 4, 1), (kname, 600.0, 2), (kname, 400.0, 2),
+                 (kname, 1500.0, 3), (kname, 500.0, 3)])
+    _counter_db(tmp_path / "w.db", "WRITE_SIZE",
+                [(copy, gib_kib, 1), (kname, 300.0, 2), (kname, 300.0, 3)])
+    rec = bench.summarize_pmc(str(tmp_path / "f.db"), str(tmp_path / "w.db"), "dense", "test command",
+                              out=str(tmp_path / "rec.json"))
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["launches"] == [2, 2]
+    # mean of (1000, 2000) KiB fetched, x2; 300 KiB written, x1
+    assert rec["hbm_fetch_bytes_per_launch"] == pytest.approx(1500 * 1024 * 2.0)
+    assert rec["hbm_write_bytes_per_launch"] == pytest.approx(300 * 1024)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(1500 * 1024 * 2 + 300 * 1024)
+    assert json.load(open(tmp_path / "rec.json")) == rec
+
+
+def test_no_kernel_in_the_database_is_an_error(bench, tmp_path):
+    _counter_db(tmp_path / "f.db", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 1.0, 1)])
+    _counter_db(tmp_path / "w.db", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1.0, 1)])
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(str(tmp_path / "f.db"), str(tmp_path / "w.db"), "dense", "c",
+                            out=str(tmp_path / "rec.json"))
+
+
+def test_traffic_is_withheld_once_the_kernel_source_changed(bench, tmp_path, monkeypatch):
+    kprefix, src, fname = bench.DOMINANT["dense"]
+    rec = {"hbm_bytes_per_launch": 123.0, "source_sha256_16": bench.src_hash(src)}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / fname).write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_for("dense") == (123.0, "profiles/" + fname)
+    rec["source_sha256_16"] = "0" * 16
+    (tmp_path / "profiles" / fname).write_text(json.dumps(rec))
+    value, why = bench.traffic_for("dense")
+    assert value is None and why.startswith("stale")
+    assert bench.traffic_for("decode") == (None, None)
