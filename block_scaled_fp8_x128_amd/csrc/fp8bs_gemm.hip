@@ -154,20 +154,24 @@ __device__ __forceinline__ bool expert_of_tile(const int32_t *offsets, int64_t E
 }
 
 // The row tiles of the grouped form, written once per launch by one wave so
-// that the GEMM workgroups look a tile up with one scalar load: expert e
-// contributes ceil(count_e / BM) tiles, in expert order; entries past the
-// last tile get e = -1, and *count receives the number of tiles, so that
-// the GEMM spreads exactly the existing tiles over the XCDs.  Offsets are
-// clamped and made non-decreasing as in expert_of_tile.  tiles_m >=
-// ceil(M_total / BM) + E bounds the count.
-template <int BM>
+// that the GEMM workgroups look a tile up with one scalar load.  Expert e's
+// rows are cut into BM_A-row tiles from its first row; the last, partial
+// tile goes to table B when it has at most BM_B rows (BM_B > 0) -- it is then
+// multiplied with BM_B-row tiles instead of padded to BM_A -- and to table A
+// otherwise.  Tiles are in expert order; entries past a table's last tile
+// get e = -1, and count[0], count[1] receive the two tables' tile counts, so
+// that each GEMM spreads exactly the existing tiles over the XCDs.  Offsets
+// are clamped and made non-decreasing as in expert_of_tile.  cap_a >=
+// ceil(M_total / BM_A) + E and cap_b >= E bound the counts.
+template <int BM_A, int BM_B>
 __global__ __launch_bounds__(64) void grouped_tile_table_kernel(const int32_t *offsets, int64_t E, int64_t M_total,
-                                                                int tiles_m, GroupTile *tab, int32_t *count)
+                                                                int cap_a, GroupTile *tab_a, int cap_b,
+                                                                GroupTile *tab_b, int32_t *count)
 {
     const int lane = threadIdx.x;
     int64_t prev_end = offsets[0];
     prev_end = prev_end < 0 ? 0 : (prev_end > M_total ? M_total : prev_end);
-    int base = 0;
+    int base_a = 0, base_b = 0;
     for (int64_t e0 = 0; e0 < E; e0 += 64) {
         const int64_t e = e0 + lane;
         int64_t end = (e < E) ? (int64_t)offsets[e + 1] : prev_end;
@@ -180,27 +184,43 @@ __global__ __launch_bounds__(64) void grouped_tile_table_kernel(const int32_t *o
         int64_t start = __shfl_up(end, 1);
         if (lane == 0)
             start = prev_end;
-        const int cnt = (e < E) ? (int)((end - start + BM - 1) / BM) : 0;
-        int inc = cnt;
+        const int64_t rows = (e < E) ? end - start : 0;
+        const int64_t rem = rows % BM_A;
+        const bool rem_b = BM_B > 0 && rem > 0 && rem <= BM_B;
+        const int cnt_a = (int)(rows / BM_A) + ((rem > 0 && !rem_b) ? 1 : 0);
+        const int cnt_b = rem_b ? 1 : 0;
+        int inc_a = cnt_a, inc_b = cnt_b; // inclusive prefix sums of the tile counts
         for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(inc, d);
-            if (lane >= d)
-                inc += o;
+            const int oa = __shfl_up(inc_a, d), ob = __shfl_up(inc_b, d);
+            if (lane >= d) {
+                inc_a += oa;
+                inc_b += ob;
+            }
         }
-        const int first = base + inc - cnt;
-        for (int j = 0; j < cnt; ++j) {
-            const int t = first + j;
-            const int64_t r0 = start + (int64_t)j * BM;
-            if (t < tiles_m)
-                tab[t] = GroupTile{r0, (int32_t)e, (int32_t)((end - r0) < BM ? (end - r0) : BM)};
+        const int first_a = base_a + inc_a - cnt_a;
+        for (int j = 0; j < cnt_a; ++j) {
+            const int t = first_a + j;
+            const int64_t r0 = start + (int64_t)j * BM_A;
+            if (t < cap_a)
+                tab_a[t] = GroupTile{r0, (int32_t)e, (int32_t)((end - r0) < BM_A ? (end - r0) : BM_A)};
         }
-        base += __shfl(inc, 63);
+        if (rem_b) {
+            const int t = base_b + inc_b - 1;
+            if (t < cap_b)
+                tab_b[t] = GroupTile{end - rem, (int32_t)e, (int32_t)rem};
+        }
+        base_a += __shfl(inc_a, 63);
+        base_b += __shfl(inc_b, 63);
         prev_end = __shfl(end, 63);
     }
-    for (int t = base + lane; t < tiles_m; t += 64)
-        tab[t] = GroupTile{0, -1, 0};
-    if (lane == 0)
-        *count = base < tiles_m ? base : tiles_m;
+    for (int t = base_a + lane; t < cap_a; t += 64)
+        tab_a[t] = GroupTile{0, -1, 0};
+    for (int t = base_b + lane; t < cap_b; t += 64)
+        tab_b[t] = GroupTile{0, -1, 0};
+    if (lane == 0) {
+        count[0] = base_a < cap_a ? base_a : cap_a;
+        count[1] = base_b < cap_b ? base_b : cap_b;
+    }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
@@ -1352,15 +1372,17 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     }
 }
 
-// Grouped workspace: the tile count, padded to 16 bytes, then the tile table.
+// Grouped workspace: the two tile counts, padded to 16 bytes, then table A
+// (256-row tiles: ceil(M_total / 256) + E entries) and table B (the experts'
+// last tiles of at most 128 rows: E entries).  Forced to 128-row tiles
+// (FP8BS_GEMM_VARIANT=dma), table A holds every tile and B stays empty.
 constexpr size_t kGroupHeader = 16;
 
-// Row tiles of the grouped form's persistent kernels (the table's length):
-// BM = 256 unless forced to 128.
-static int64_t grouped_tiles_m(int64_t E, int64_t M_total)
+static bool grouped_small_tiles() { return forced_variant() == V_DMA; }
+
+static int64_t grouped_cap_a(int64_t E, int64_t M_total)
 {
-    const int fv = forced_variant();
-    const int64_t bm = (fv == V_DMA) ? 128 : 256;
+    const int64_t bm = grouped_small_tiles() ? 128 : 256;
     return (M_total + bm - 1) / bm + E;
 }
 
@@ -1368,7 +1390,7 @@ size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K)
 {
     if (E <= 0 || M_total <= 0 || forced_variant() == V_SIMPLE || !dma_ok(N, K))
         return 0;
-    return kGroupHeader + (size_t)grouped_tiles_m(E, M_total) * sizeof(GroupTile);
+    return kGroupHeader + (size_t)(grouped_cap_a(E, M_total) + E) * sizeof(GroupTile);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
@@ -1389,23 +1411,35 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
     a.K = K;
     a.E = E;
     a.ksplit = 1;
-    const int fv = forced_variant();
     if (grouped_workspace_size(E, M_total, N, K) > 0) {
-        a.tiles_m = (int)grouped_tiles_m(E, M_total);
-        a.tiles_n = (int)(N / 256);
+        const int cap_a = (int)grouped_cap_a(E, M_total), cap_b = (int)E;
         int32_t *count = (int32_t *)workspace;
-        GroupTile *tab = (GroupTile *)((uint8_t *)workspace + kGroupHeader);
-        a.gtab = tab;
-        a.gcount = count;
-        const bool big = fv != V_DMA;
-        hipError_t e = big ? launch(grouped_tile_table_kernel<256>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
-                                    a.tiles_m, tab, count)
-                           : launch(grouped_tile_table_kernel<128>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
-                                    a.tiles_m, tab, count);
+        GroupTile *tab_a = (GroupTile *)((uint8_t *)workspace + kGroupHeader);
+        GroupTile *tab_b = tab_a + cap_a;
+        a.tiles_n = (int)(N / 256);
+        if (grouped_small_tiles()) {
+            hipError_t e = launch(grouped_tile_table_kernel<128, 0>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
+                                  cap_a, tab_a, cap_b, tab_b, count);
+            if (e != hipSuccess)
+                return e;
+            a.tiles_m = cap_a;
+            a.gtab = tab_a;
+            a.gcount = count;
+            return run_dma<128, 256, 2, 4, true>(a, out_fp32 != 0, pow2 != 0, stream);
+        }
+        hipError_t e = launch(grouped_tile_table_kernel<256, 128>, dim3(1), dim3(64), 0, stream, offsets, E, M_total,
+                              cap_a, tab_a, cap_b, tab_b, count);
         if (e != hipSuccess)
             return e;
-        if (big)
-            return run_dma<256, 256, 4, 2, true>(a, out_fp32 != 0, pow2 != 0, stream);
+        // 256-row tiles first, then the experts' short last tiles with 128-row tiles
+        a.tiles_m = cap_a;
+        a.gtab = tab_a;
+        a.gcount = count;
+        if ((e = run_dma<256, 256, 4, 2, true>(a, out_fp32 != 0, pow2 != 0, stream)) != hipSuccess)
+            return e;
+        a.tiles_m = cap_b;
+        a.gtab = tab_b;
+        a.gcount = count + 1;
         return run_dma<128, 256, 2, 4, true>(a, out_fp32 != 0, pow2 != 0, stream);
     }
     a.tiles_m = (int)((M_total + 127) / 128 + E);

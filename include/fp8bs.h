@@ -171,11 +171,12 @@ FP8BS_API int fp8_block_gemm(const void *xq, const float *xs, const void *wq, co
  *     out-of-bounds access (the result is then unspecified).
  *   y [M_total, N]: row r holds fp8_block_gemm of row r with its expert.
  * Workspace: fp8bs_grouped_workspace_size(E, M_total, N, K) bytes: 16 for
- *   the number of row tiles, then 16 per row tile (at most ceil(M_total / 256)
- *   + E tiles).  The call first writes that count and the table of (expert,
- *   first row, row count) of every row tile there from group_offsets, on the
- *   device.  It need not be zeroed; calls that share a workspace must not
- *   overlap in time.
+ *   the row-tile counts, then 16 per row tile: at most ceil(M_total / 256) + E
+ *   tiles of 256 rows and E short last tiles (an expert's last <= 128 rows,
+ *   multiplied with 128-row tiles instead of padded to 256).  The call first
+ *   writes the counts and the tables of (expert, first row, row count) there
+ *   from group_offsets, on the device.  It need not be zeroed; calls that
+ *   share a workspace must not overlap in time.
  * Errors: as fp8_block_gemm; INVALID_ARG if E <= 0 with M_total > 0.
  */
 FP8BS_API int fp8_block_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,

@@ -60,9 +60,9 @@ def test_workspace_queries_are_pure(fp8bs):
     L = fp8bs.lib()
     assert L.fp8bs_gemm_workspace_size(0, 128, 128) == 0
     assert L.fp8bs_gemm_workspace_size(-1, 128, 128) == 0
-    # grouped: a 16-byte tile count, then the row-tile table, 16 bytes per 256-row tile (at most
-    # ceil(M_total / 256) + E tiles)
-    assert L.fp8bs_grouped_workspace_size(128, 65536, 1536, 2048) == 16 + 16 * (65536 // 256 + 128)
+    # grouped: 16 bytes of tile counts, then two row-tile tables of 16-byte entries: the 256-row
+    # tiles (at most ceil(M_total / 256) + E) and the experts' short last tiles (at most E)
+    assert L.fp8bs_grouped_workspace_size(128, 65536, 1536, 2048) == 16 + 16 * (65536 // 256 + 128 + 128)
     assert L.fp8bs_grouped_workspace_size(0, 65536, 1536, 2048) == 0
     # dense: fp32 partial sums (ksplit slices of M x N) when the product is split along K,
     # never for products with at least one 256 x 256 tile per compute unit
