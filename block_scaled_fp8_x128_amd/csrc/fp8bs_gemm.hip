@@ -24,11 +24,21 @@
 // lane holding 4 consecutive n of one m -- one 16-byte (fp32) or 8-byte
 // (bf16) store per MFMA tile.
 //
-// Staging.  Global -> registers -> LDS, double-buffered, one barrier per K
-// block; the next block's global loads are in flight while the current one
-// is multiplied.  LDS rows are 128 bytes; the 16-byte chunk c of row r is
-// stored at chunk c ^ ((r >> 1) & 7), so the 16 rows read by one 16-lane
-// group spread over all banks.
+// Kernels in this file:
+//   gemm_dma_kernel       the persistent large-tile GEMM (256x256 or 128x256
+//                         tiles, operands loaded straight into LDS), also split
+//                         along K for few-tile products, grouped over experts,
+//                         and with power-of-2 scales applied by the matrix core;
+//   splitk_reduce_kernel  adds the K ranges of a split product;
+//   grouped_tile_table_kernel  the row tiles of a grouped launch;
+//   gemm_skinny_kernel    weight streaming for at most 16 activation rows;
+//   gemm_kernel           the general 128x128 GEMM (N not a multiple of 256):
+//                         global -> registers -> LDS, double-buffered, one
+//                         barrier per K block; LDS rows are 128 bytes and the
+//                         16-byte chunk c of row r sits at chunk c ^ ((r >> 1)
+//                         & 7), so the 16 rows one 16-lane group reads spread
+//                         over all banks.
+// The launchers at the end pick one per shape (the variant table).
 //
 // Workgroup order.  Consecutive workgroup ids are dispatched round-robin to
 // the 8 XCDs, each with its own L2; ids are remapped so that each XCD gets a
@@ -388,12 +398,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
 // ---- large-tile kernels: direct global->LDS loads -------------------------------
 //
 // Same product as gemm_kernel, organized for the dense prefill/training
-// shapes (M in the thousands):
-//   - large workgroup tiles (BM x BN = 256 x 256 over 8 waves, or 128 x 256
-//     over 4) of 64 x 128 wave tiles, so each K block moves (BM + BN) * 128
-//     bytes for 2 * BM * BN * 128 FLOP and each wave reads 24 KiB of LDS per
-//     32 MFMAs.  With 8 waves each SIMD holds two, so one wave's fp32 rescale
-//     (VALU) runs while the other's MFMAs keep the matrix core busy;
+// shapes (M in the thousands) and, split along K, for the few-row ones:
+//   - large workgroup tiles, 256 x 256 over 8 waves of 64 x 128 (each wave
+//     reads 24 KiB of LDS per 32 MFMAs) or 128 x 256 over 8 waves of 64 x 64,
+//     so each K block moves (BM + BN) * 128 bytes for 2 * BM * BN * 128 FLOP.
+//     With 8 waves each SIMD holds two, so one wave's fp32 rescale (VALU)
+//     runs while the other's MFMAs keep the matrix core busy;
 //   - operands and activation scales go from global memory straight into LDS
 //     (buffer_load ... lds: each dwordx4 wave instruction fills 1 KiB = 8 LDS
 //     rows of 128 bytes, lane i writing bytes 16i .. 16i+15), so no VGPRs or
@@ -409,9 +419,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
 //     so the layout is produced on the global side: the lane that fills LDS
 //     row p, slot s fetches the chunk s ^ (r & 7) of the tile row r stored
 //     there -- still 8 lanes per 128-byte row, fully coalesced;
-//   - STAGES LDS buffers: the loads of block kb + STAGES - 1 are in flight
-//     while block kb is multiplied; one barrier per K block both publishes
-//     block kb and retires the reads of the buffer the next loads refill.
+//   - STAGES LDS buffers (two for 256 x 256, three for 128 x 256: what fits
+//     in 160 KiB): the loads of the next STAGES - 1 K blocks are in flight
+//     while a block is multiplied; one barrier per K block both publishes the
+//     next block and retires the reads of the buffer the next loads refill.
 //     Waits are explicit (s_waitcnt vmcnt with the count of loads issued after
 //     the ones needed), with every count a compile-time constant;
 //   - the weight scale of a K block is one scalar load; each wave fetches the
@@ -528,14 +539,14 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, T
     return true;
 }
 
-// Persistent form: gridDim.x workgroups (one per CU) walk the virtual tiles
-// v = blockIdx.x, blockIdx.x + gridDim.x, ...  All (tile, K block) steps of
-// a workgroup form one stream through the two LDS stages: the operands of
-// step s + 2 are issued in the middle of step s, as soon as every wave has
-// finished reading the stage they refill (a full step of lookahead), and the
-// fragments of step s + 1 are read into registers during the last MFMA
-// groups of step s, so the matrix cores never wait on LDS at a step
-// boundary; a tile's output stores drain while the next tile computes.  Stores are buffer stores
+// Persistent form: gridDim.x workgroups (one per CU) walk the virtual work
+// units v = blockIdx.x, blockIdx.x + gridDim.x, ...  All (unit, K block)
+// steps of a workgroup form one stream through the LDS stages: the operands
+// of step s + STAGES are issued during the last MFMA groups of step s, as
+// soon as every wave has finished reading the stage they refill, and the
+// fragments of step s + 1 are read into registers during those same groups,
+// so the matrix cores never wait on LDS at a step boundary; a unit's output
+// stores drain while the next unit computes.  Stores are buffer stores
 // whose out-of-range rows the hardware drops.  SPLIT: the work units are
 // (tile, K range) pairs and each writes its fp32 partial tile to the
 // partial-sum buffer (ksplit slices of M x N), summed by splitk_reduce_kernel.
@@ -842,9 +853,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 
     // Pipeline.  While step s is computed from stage s % STAGES, the loads of
     // steps s + 1 .. s + STAGES - 1 are in flight (or landed) in the other
-    // stages; those of step s + STAGES are issued right after the barrier in
-    // the middle of step s, the earliest point at which every wave has
-    // finished reading the stage they refill.  Every pipeline slot issues its
+    // stages; those of step s + STAGES are issued after the barrier near the
+    // end of step s, the earliest point at which every wave has finished
+    // reading the stage they refill.  Every pipeline slot issues its
     // loads -- on empty ranges past the end of the stream -- so the wait
     // counts stay exact.  Per step in flight only a flag and the address of
     // its weight scale are carried; the tile of the step being computed
