@@ -59,6 +59,8 @@ SMALL = [
     # products split along K (fewer output tiles than compute units): 16 ranges of 4 blocks, uneven
     # ranges of 4 and 5 blocks (K/128 = 23), and 256-row tiles with a ragged second row tile
     (40, 512, 8192), (97, 512, 2944), (300, 512, 4096),
+    # a few rows with K past the weight-streaming kernel's 16384: the persistent kernel, 32 K ranges
+    (3, 256, 32768),
 ]
 
 
