@@ -427,7 +427,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
 //     the ones needed), with every count a compile-time constant;
 //   - the weight scale of a K block is one scalar load; each wave fetches the
 //     activation scales of its own 64 rows (one dword per lane) with its
-//     operands, into a region of the stage that only it reads.
+//     operands, into a region of the stage that only it reads;
+//   - bf16 output leaves through a per-wave LDS staging area after the
+//     stages (16 rows x EPI_CW columns, rows padded by 16 bytes), so each
+//     store instruction writes whole 64- or 128-byte row segments instead of
+//     16 scattered 32-byte pieces.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES_>
 struct DmaCfg {
     static constexpr int NW = WAVES_M * WAVES_N;
@@ -449,6 +453,13 @@ struct DmaCfg {
     static_assert(WN % 16 == 0, "wave tile must be made of 16x16 MFMA tiles");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-wide weight scale block");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
+    // output staging: 64 bf16 columns per row where they fit, else 32
+    static constexpr int EPI_CW = STAGES * STAGE_BYTES + NW * 16 * (64 * 2 + 16) <= 160 * 1024 ? 64 : 32;
+    static constexpr int EPI_RS = EPI_CW * 2 + 16;
+    static constexpr int EPI_BYTES = NW * 16 * EPI_RS;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + EPI_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU (stages and output staging)");
+    static_assert(WN % EPI_CW == 0 && EPI_BYTES % 1024 == 0, "output staging chunks");
 };
 
 // LDS row of tile row r, and the tile row held by LDS row p (inverse maps).
@@ -563,7 +574,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // three LDS stages (two steps of loads in flight) where they fit
     constexpr int NST = 3 * DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>::STAGE_BYTES <= 160 * 1024 ? 3 : 2;
     using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, NST>;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::STAGES * C::STAGE_BYTES];
+    // one array: the operand stages, then the output staging area (two
+    // separate __shared__ arrays made the main loop run at half speed)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -573,6 +586,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     const int ntiles = a.tiles_m * a.tiles_n * (SPLIT ? a.ksplit : 1); // work units
     const int sub = lane >> 3, slot = lane & 7;
     const int fr = lane & 15, fg = lane >> 4;
+    uint8_t *const epi_lds = lds + C::STAGES * C::STAGE_BYTES + wave * 16 * C::EPI_RS; // this wave's staging rows
 
     // ---- DMA cursor: the tile and K block whose operands load next ----
     int dv = blockIdx.x;
@@ -730,12 +744,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // fragment registers for the next step's.  (For the last step of a
     // workgroup those reads fetch data that is never used; the barrier is
     // uniform.)
-    auto compute = [&](int stage, int nstage, bool full_wait, float sw_next, auto &&load_q)
+    auto compute = [&](int stage, int nstage, bool full_wait, const CONST_AS float *swp, auto &&load_q)
                        __attribute__((always_inline)) {
         const uint8_t *L = lds + stage * C::STAGE_BYTES;
         const uint8_t *Ln = lds + nstage * C::STAGE_BYTES;
         v4f part[2];
         float xs_next[C::TM];
+        float sw_next = 0.f;
         // POW2: the E8M0 code of each row tile's scale product (its biased
         // exponent; the product of two powers of two is exact in fp32).  Lane
         // l's scale applies to the activation row l % 16 whose fragment it
@@ -762,6 +777,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                     wait_vmcnt<(C::STAGES - 2) * C::DPW>();
                 wait_lgkmcnt0();
                 sync();
+                // the next step's weight scale (a valid address even past the
+                // end of the stream, where the value goes unused): no wait for
+                // an LDS read falls between here and the end of the step, where
+                // the reads issued below are waited for anyway, so the scalar
+                // load's out-of-order return costs nothing
+                sw_next = *swp;
                 awq[(j + 2) % 3] = frag(Ln + wo[0], Ln + wo[1]);
 #pragma unroll
                 for (int i = 0; i < C::TM; ++i)
@@ -823,6 +844,41 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         constexpr int ES = F32 ? 4 : 2;
         const __amdgpu_buffer_rsrc_t yr =
             make_rsrc(base + (g.row_begin * N + g.n0) * ES, (g.row_end - g.row_begin) * N * ES);
+        if constexpr (!F32) {
+            // per 16-row tile and EPI_CW-column chunk: each lane writes its 4
+            // columns of each MFMA tile into the wave's staging rows, then reads
+            // back 16 contiguous bytes of one row, so LPR lanes cover a whole
+            // row segment of the store (LDS reads and writes of one wave
+            // complete in order, so no barrier is needed)
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            constexpr int LPR = C::EPI_CW * 2 / 16; // lanes per staged row
+            constexpr int RPI = 64 / LPR;           // rows per read-back
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+                for (int c = 0; c < C::WN / C::EPI_CW; ++c) {
+#pragma unroll
+                    for (int jj = 0; jj < C::EPI_CW / 16; ++jj) {
+                        const int j = c * (C::EPI_CW / 16) + jj;
+                        const v4f v = acc[i][j];
+                        const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
+                        const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
+                        *(u32x2 *)(epi_lds + fr * C::EPI_RS + jj * 32 + fg * 8) =
+                            u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+                        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                    for (int h = 0; h < 16 / RPI; ++h) {
+                        const int r = h * RPI + lane / LPR, cc = lane % LPR;
+                        const u32x4 d = *(const u32x4 *)(epi_lds + r * C::EPI_RS + cc * 16);
+                        const int m = wm * C::WM + i * 16 + r;
+                        const int n = wn * C::WN + c * C::EPI_CW + cc * 8;
+                        __builtin_amdgcn_raw_buffer_store_b128(d, yr, (int)(((int64_t)m * N + n) * 2), 0, 0);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
             const int m = wm * C::WM + i * 16 + fr;
@@ -830,16 +886,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             for (int j = 0; j < C::TN; ++j) {
                 const int n = wn * C::WN + j * 16 + fg * 4;
                 const int off = (int)(((int64_t)m * N + n) * ES);
-                const v4f v = acc[i][j];
-                if constexpr (F32) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yr, off, 0, 0);
-                } else {
-                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-                    const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
-                    const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)}, yr, off, 0, 0);
-                }
+                // fp32 (a split product's partial tile, or fp32 output): each
+                // lane's 16 bytes, 4 lanes per 64-byte row segment
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), yr, off, 0, 0);
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -905,15 +954,6 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     while (true) {
         if (advance)
             dmore = dma_next();
-        float sw_next = 0.f;
-        if (has1) {
-            sw_next = *wsp1;
-            // Take the scalar load's result right away: loads through the
-            // scalar cache may return out of order, so while one is
-            // outstanding every wait for an LDS read has to be lgkmcnt(0),
-            // which would also wait for the fragment reads issued ahead.
-            asm volatile("" ::"s"(sw_next));
-        }
         const bool hasS = dmore; // step s + STAGES exists
         const int64_t kbS = dkb;
         const CONST_AS float *wspS = hasS ? ws_of(dt) + dkb : (C::STAGES == 3 ? wsp2 : wsp1);
@@ -921,7 +961,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         // only the loads go in the middle of the MFMA stream; the cursor
         // advances (and sets up the next tile's loads) at the top of the
         // next step
-        compute(stage, nstage, stored, sw_next, [&](int q) { issue_q(q, kbS, stage, hasS); });
+        compute(stage, nstage, stored, wsp1, [&](int q) { issue_q(q, kbS, stage, hasS); });
         advance = hasS;
         stage = nstage;
         stored = false;
