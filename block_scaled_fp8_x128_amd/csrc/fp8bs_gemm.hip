@@ -804,11 +804,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 else
                     part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         aw, bx[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                // issue order, fenced: each MFMA, then the rescale of the
-                // previous one (whose product has had a full MFMA to land),
-                // and in the last group the next step's X fragment it freed;
-                // after the barrier, the next loads one or two per MFMA
-                __builtin_amdgcn_sched_barrier(0);
+                // issue order: each MFMA, then the rescale of the previous
+                // one (whose product has had a full MFMA to land), and in the
+                // last group the next step's X fragment it freed; after the
+                // barrier, the next loads one or two per MFMA.  Only the last
+                // two groups, which carry the loads, are fenced per MFMA;
+                // elsewhere the scheduler may interleave MFMAs and rescales
+                // (about 1% faster than fencing every MFMA)
+                if (j + 2 >= C::TN)
+                    __builtin_amdgcn_sched_barrier(0);
                 if (!POW2 && t > 0)
                     rescale(t - 1, part[(t - 1) & 1]);
                 if (last)
@@ -820,7 +824,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                         if (q * 2 * C::TM / C::DPW == slot_i)
                             load_q(q);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                if (j + 2 >= C::TN)
+                    __builtin_amdgcn_sched_barrier(0);
             }
         }
         if constexpr (!POW2)
