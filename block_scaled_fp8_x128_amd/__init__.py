@@ -39,6 +39,9 @@ EXPORTS = (
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_pow2",
     "fp8_block_grouped_gemm_pow2",
+    "fp8_block_linear",
+    "fp8_block_linear_pow2",
+    "fp8bs_linear_workspace_size",
     "fp8bs_gemm_workspace_size",
     "fp8bs_grouped_workspace_size",
     "fp8bs_status_string",
@@ -69,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.fp8_block_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_gemm_pow2.argtypes = L.fp8_block_gemm.argtypes
         L.fp8_block_grouped_gemm_pow2.argtypes = L.fp8_block_grouped_gemm.argtypes
+        L.fp8_block_linear.argtypes = [P, P, P, I64, I64, I64, P, I32, P, SZ, P]
+        L.fp8_block_linear_pow2.argtypes = L.fp8_block_linear.argtypes
+        L.fp8bs_linear_workspace_size.argtypes = [I64, I64, I64]
+        L.fp8bs_linear_workspace_size.restype = SZ
         L.fp8bs_gemm_workspace_size.argtypes = [I64, I64, I64]
         L.fp8bs_gemm_workspace_size.restype = SZ
         L.fp8bs_grouped_workspace_size.argtypes = [I64, I64, I64, I64]
@@ -77,7 +84,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
         for fn in ("quant_act_1x128", "quant_w_128x128", "quant_w_128x128_batched", "fp8_block_gemm",
-                   "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2"):
+                   "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
+                   "fp8_block_linear", "fp8_block_linear_pow2"):
             getattr(L, fn).restype = I32
         _lib = L
     return _lib
@@ -228,6 +236,41 @@ def _gemm(fn, xq, xs, wq, ws, out_dtype, out, workspace):
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code,
                             _ptr(workspace), wsz, _stream(xq))
+    _check(fn, st)
+    return out
+
+
+def linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().fp8bs_linear_workspace_size(M, N, K))
+
+
+def fp8_block_linear(x, wq, ws, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """Y [M, N] = fp8_block_gemm(quant_act_1x128(x), wq, ws) from bf16 x [M, K] (one launch for decode rows)."""
+    return _linear("fp8_block_linear", x, wq, ws, out_dtype, out, workspace)
+
+
+def fp8_block_linear_pow2(x, wq, ws, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """fp8_block_linear with x quantized to power-of-2 scales (ws must hold POW2 scales)."""
+    return _linear("fp8_block_linear_pow2", x, wq, ws, out_dtype, out, workspace)
+
+
+def _linear(fn, x, wq, ws, out_dtype, out, workspace):
+    x = _bf16_payload(x, "x")
+    wq, ws = _codes(wq, "wq"), _f32(ws, "ws")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or ws.shape != (N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=x.device)
+    need = linear_workspace_size(M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = getattr(lib(), fn)(_ptr(x), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code, _ptr(workspace), wsz, _stream(x))
     _check(fn, st)
     return out
 

@@ -64,7 +64,7 @@ int check_quant(const void *x, int64_t R, int64_t K, const void *q, const float 
     return FP8BS_OK;
 }
 
-int check_gemm_common(const void *xq, const float *xs, const void *y, int64_t M, int64_t N, int64_t K, int out_dtype)
+int check_gemm_shape(int64_t M, int64_t N, int64_t K, int out_dtype)
 {
     if (M < 0 || N <= 0 || K <= 0 || (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_FP32))
         return FP8BS_INVALID_ARG;
@@ -75,6 +75,14 @@ int check_gemm_common(const void *xq, const float *xs, const void *y, int64_t M,
     // output tiles are counted in 32-bit integers (work units, grid sizes)
     if (((M + 127) / 128) * (N / 128) >= kMaxDim)
         return FP8BS_UNSUPPORTED_SHAPE;
+    return FP8BS_OK;
+}
+
+int check_gemm_common(const void *xq, const float *xs, const void *y, int64_t M, int64_t N, int64_t K, int out_dtype)
+{
+    const int st = check_gemm_shape(M, N, K, out_dtype);
+    if (st != FP8BS_OK)
+        return st;
     if (!tensor_ok(xq, M * K, 16) || !tensor_ok(xs, M * K, 4) || !tensor_ok(y, M * N, 16))
         return FP8BS_INVALID_ARG;
     return FP8BS_OK;
@@ -231,6 +239,51 @@ static int grouped_impl(const void *xq, const float *xs, const void *wq, const f
         return st;
     return status_of(fp8bs::launch_grouped_gemm(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y,
                                                 out_dtype == FP8BS_OUT_FP32, pow2, workspace, (hipStream_t)stream));
+}
+
+size_t fp8bs_linear_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    return fp8bs::linear_workspace_size(M, N, K);
+}
+
+static int linear_impl(const void *x, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                       int out_dtype, int pow2, void *workspace, size_t workspace_bytes, void *stream)
+{
+    // the GEMM's shape checks, the activation quantizer's grid limit, then
+    // the pointers (x [M, K] bf16 takes the place of xq and xs)
+    int st = check_gemm_shape(M, N, K, out_dtype);
+    if (st != FP8BS_OK)
+        return st;
+    if (M * (K / 128) >= kMaxDim * 64)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (!tensor_ok(x, M * K, 16) || !tensor_ok(y, M * N, 16) || !tensor_ok(wq, N * K, 16) ||
+        !tensor_ok(ws, N * K, 4))
+        return FP8BS_INVALID_ARG;
+    if (M == 0)
+        return FP8BS_OK;
+    const size_t need = fp8bs::linear_workspace_size(M, N, K);
+    if (workspace_bytes < need)
+        return FP8BS_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+        return FP8BS_INVALID_ARG;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_linear(x, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, pow2, workspace,
+                                          (hipStream_t)stream));
+}
+
+int fp8_block_linear(const void *x_bf16, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                     int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return linear_impl(x_bf16, wq, ws, M, N, K, y, out_dtype, 0, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_linear_pow2(const void *x_bf16, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+                          void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return linear_impl(x_bf16, wq, ws, M, N, K, y, out_dtype, 1, workspace, workspace_bytes, stream);
 }
 
 int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,

@@ -1007,11 +1007,22 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 // order, so results are deterministic) and written out.
 constexpr int kSkinnyMaxIt = 16; // K blocks per wave of the weight-streaming kernel (K <= 16384)
 
-template <int TM, int TN, int D, bool OUT_F32>
+//
+// QX = 0: X arrives quantized (a.xq codes, a.xs scales).  QX = 1 / 2: a.xq
+// holds bf16 activations, and each wave quantizes the fragments it loads with
+// the 1x128 activation quantizer's own encoder (EXACT / POW2 scales): a
+// lane's 32 consecutive K values of one row are a quarter of a 128-value
+// block, whose other quarters sit 16 and 32 lanes away, so two lane
+// exchanges give the block's amax.  The codes and scales are bit for bit
+// those quant_act_1x128 writes, so Y is that of quant_act_1x128 followed by
+// this kernel.
+template <int TM, int TN, int D, bool OUT_F32, int QX>
 __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
 {
     constexpr int NW = 8;
-    constexpr int LPB = 2 * TN + 3 * TM + 1; // loads per K block: W lo/hi, X lo/hi, X scale, W scale
+    constexpr int XB = QX ? 2 : 1; // bytes per X element as loaded
+    // loads per K block: W lo/hi, X (lo/hi and a scale, or four bf16 chunks), W scale
+    constexpr int LPB = 2 * TN + (QX ? 4 * TM : 3 * TM) + 1;
     static_assert((D - 1) * LPB < 64, "outstanding loads must fit the vmcnt field");
     // (rows padded by 16 bytes: the 16 rows a 16-lane group writes then fall
     // in different banks)
@@ -1029,7 +1040,7 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
     // m0 .. m0 + mrows - 1.  Lane offsets: row fr of a 16-row tile, bytes
     // 32 fg .. 32 fg + 31 of the K block (the same K order for both operands).
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wq + n0 * K, (int64_t)TN * 16 * K);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.xq + m0 * K, mrows * K);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.xq + m0 * K * XB, mrows * K * XB);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.xs + m0 * KB, mrows * KB * 4);
     const __amdgpu_buffer_rsrc_t none = make_rsrc(a.xq, 0);
     // the weight scales of this tile's 128-row block, loaded with the operands
@@ -1043,6 +1054,7 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
 
     v8i wf[D][TN], xf[D][TM];
     float xv[D][TM], wv[D];
+    u32x4 xb[QX ? D : 1][TM][4]; // bf16 X: bytes 64 fg .. 64 fg + 63 of the row's K block
     // Loads of this wave's it-th K block into ring slot `slot`.  Blocks past
     // the end issue the same instructions on an empty range (no traffic), so
     // every step issues LPB loads and the waits below are fixed counts.
@@ -1061,6 +1073,16 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
         }
         // (the X row of a lane is in the per-lane offset, so a row past M
         // is out of range however the hardware counts the scalar offset)
+        if constexpr (QX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int vo = 2 * loff + (int)(i * 16 * K * 2);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    xb[slot][i][c] = __builtin_amdgcn_raw_buffer_load_b128(x_, vo + 16 * c, kb * BK * 2, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int vo = loff + (int)(i * 16 * K);
@@ -1090,6 +1112,28 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a)
     for (int it = 0; it < kSkinnyMaxIt; ++it) {
         const int d = it % D;
         wait_vmcnt<(D - 1) * LPB>(); // block `it` landed; D - 1 younger blocks may fly
+        if constexpr (QX) {
+            constexpr int MODE = QX - 1;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                uint32_t mag = chunk_max_mag(xb[d][i][0]);
+#pragma unroll
+                for (int c = 1; c < 4; ++c) {
+                    const uint32_t m = chunk_max_mag(xb[d][i][c]);
+                    mag = mag > m ? mag : m;
+                }
+                uint32_t o = (uint32_t)__shfl_xor((int)mag, 16);
+                mag = mag > o ? mag : o;
+                o = (uint32_t)__shfl_xor((int)mag, 32);
+                mag = mag > o ? mag : o;
+                BlockQuant<MODE> bq;
+                bq.init(amax_value(mag));
+                const u32x2 c0 = quant_chunk<MODE>(xb[d][i][0], bq), c1 = quant_chunk<MODE>(xb[d][i][1], bq);
+                const u32x2 c2 = quant_chunk<MODE>(xb[d][i][2], bq), c3 = quant_chunk<MODE>(xb[d][i][3], bq);
+                xf[d][i] = v8i{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y, (int)c2.x, (int)c2.y, (int)c3.x, (int)c3.y};
+                xv[d][i] = bq.s;
+            }
+        }
         const float sw = wv[d];
         float sc[TM];
 #pragma unroll
@@ -1294,13 +1338,26 @@ static bool skinny_ok(int64_t M, int64_t N, int64_t K)
 // on the decode shapes).
 constexpr int64_t kSkinnyMaxM = 16;
 
-template <int TM, int TN, int D>
+template <int TM, int TN, int D, int QX = 0>
 static hipError_t run_skinny_t(GemmArgs a, bool out_f32, hipStream_t stream)
 {
     const dim3 grid((unsigned)(a.N / (TN * 16)), (unsigned)((a.M + TM * 16 - 1) / (TM * 16)));
     if (out_f32)
-        return launch(gemm_skinny_kernel<TM, TN, D, true>, grid, dim3(512), 0, stream, a);
-    return launch(gemm_skinny_kernel<TM, TN, D, false>, grid, dim3(512), 0, stream, a);
+        return launch(gemm_skinny_kernel<TM, TN, D, true, QX>, grid, dim3(512), 0, stream, a);
+    return launch(gemm_skinny_kernel<TM, TN, D, false, QX>, grid, dim3(512), 0, stream, a);
+}
+
+// The weight-streaming kernel on bf16 activations (M <= 16: one 16-row X
+// tile), quantizing them itself with EXACT (QX = 1) or POW2 (QX = 2) scales.
+template <int QX>
+static hipError_t run_skinny_qx(GemmArgs a, bool out_f32, hipStream_t stream)
+{
+    const int64_t N = a.N;
+    if (N % 64 == 0 && N / 64 >= 256)
+        return run_skinny_t<1, 4, 4, QX>(a, out_f32, stream);
+    if (N % 32 == 0 && N / 32 >= 256)
+        return run_skinny_t<1, 2, 4, QX>(a, out_f32, stream);
+    return run_skinny_t<1, 1, 6, QX>(a, out_f32, stream);
 }
 
 // W tile width: the widest of 64 / 32 / 16 rows that still gives at least 256
@@ -1429,6 +1486,50 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     default:
         return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
     }
+}
+
+// ---- the whole linear layer: bf16 activations in ---------------------------------
+//
+// Y = fp8_block_gemm(quant_act_1x128(X), Wq, Ws).  Decode shapes (at most 16
+// rows, on shapes the weight-streaming kernel takes) run as one launch that
+// quantizes X inside the GEMM; every other shape quantizes X into the
+// workspace and runs the GEMM on it.  Either way the codes, scales and Y are
+// those of the two separate calls.
+static bool linear_fused(int64_t M, int64_t N, int64_t K) { return M <= kSkinnyMaxM && skinny_ok(M, N, K); }
+
+static size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
+
+size_t linear_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || linear_fused(M, N, K))
+        return 0;
+    return align16((size_t)M * (size_t)K) + align16((size_t)M * (size_t)(K / BK) * sizeof(float)) +
+           gemm_workspace_size(M, N, K);
+}
+
+hipError_t launch_linear(const void *x, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                         int out_fp32, int pow2, void *workspace, hipStream_t stream)
+{
+    if (M == 0)
+        return hipSuccess;
+    if (linear_fused(M, N, K)) {
+        GemmArgs a = {};
+        a.xq = (const uint8_t *)x; // bf16 activations
+        a.wq = (const uint8_t *)wq;
+        a.ws = ws;
+        a.y = y;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        return pow2 ? run_skinny_qx<2>(a, out_fp32 != 0, stream) : run_skinny_qx<1>(a, out_fp32 != 0, stream);
+    }
+    uint8_t *xq = (uint8_t *)workspace;
+    float *xs = (float *)(xq + align16((size_t)M * (size_t)K));
+    void *gws = (uint8_t *)xs + align16((size_t)M * (size_t)(K / BK) * sizeof(float));
+    const hipError_t e = launch_quant_act(x, M, K, xq, xs, pow2 ? SCALE_POW2 : SCALE_EXACT, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch_gemm(xq, xs, wq, ws, M, N, K, y, out_fp32, pow2, gws, stream);
 }
 
 // Grouped workspace: the two tile counts, padded to 16 bytes, then table A

@@ -49,6 +49,11 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 // through the matrix cores' E8M0 operands where they can)
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
                        int64_t K, void *y, int out_fp32, int pow2, void *workspace, hipStream_t stream);
+// Y = fp8_block_gemm(quant_act_1x128(x), Wq, Ws) from bf16 x; the workspace
+// holds the quantized x (unless the shape runs fused) and the GEMM's own.
+size_t linear_workspace_size(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear(const void *x, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                         int out_fp32, int pow2, void *workspace, hipStream_t stream);
 size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,

@@ -19,55 +19,6 @@
 
 namespace fp8bs {
 
-// Per-block quotient state: the fast path (Newton division / exact multiply)
-// or, for the rare blocks outside its window, IEEE division.
-template <int MODE>
-struct BlockQuant {
-    float s;    // dequantization scale
-    float inv;  // POW2: 2^-k
-    Divider d;  // EXACT
-    bool fast;
-
-    __device__ __forceinline__ void init(float amax)
-    {
-        s = block_scale<MODE>(amax);
-        if (MODE == SCALE_POW2) {
-            // 2^-k is a normal fp32 for k in [-126, 127]; k never exceeds 120
-            // for finite bf16 amax, so only tiny blocks miss the fast path.
-            int k = (amax > 0.0f) ? pow2_exponent(amax) : 0;
-            fast = k >= -126;
-            inv = fast ? exp2_int(-k) : 1.0f;
-        } else {
-            fast = divider_ok(s);
-            d.init(fast ? s : 1.0f);
-        }
-    }
-    __device__ __forceinline__ float q_fast(float x) const
-    {
-        if (MODE == SCALE_POW2)
-            return x * inv; // x * 2^-k == x / s exactly, rounded once (subnormals kept)
-        return d.div(x);
-    }
-};
-
-// 8 bf16 values (one 16-byte chunk) -> 8 codes.
-template <int MODE>
-__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, const BlockQuant<MODE> &bq)
-{
-    float x0 = bf16_lo(v.x), x1 = bf16_hi(v.x), x2 = bf16_lo(v.y), x3 = bf16_hi(v.y);
-    float x4 = bf16_lo(v.z), x5 = bf16_hi(v.z), x6 = bf16_lo(v.w), x7 = bf16_hi(v.w);
-    u32x2 out;
-    if (bq.fast) {
-        out.x = pack4_e4m3(bq.q_fast(x0), bq.q_fast(x1), bq.q_fast(x2), bq.q_fast(x3));
-        out.y = pack4_e4m3(bq.q_fast(x4), bq.q_fast(x5), bq.q_fast(x6), bq.q_fast(x7));
-    } else {
-        const float s = bq.s;
-        out.x = pack4_e4m3(x0 / s, x1 / s, x2 / s, x3 / s);
-        out.y = pack4_e4m3(x4 / s, x5 / s, x6 / s, x7 / s);
-    }
-    return out;
-}
-
 // ---- activations: 1x128 blocks ------------------------------------------------
 //
 // A row-major [M, K] tensor with K % 128 == 0 is a flat sequence of

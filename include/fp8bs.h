@@ -210,6 +210,42 @@ FP8BS_API int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const
                                           int64_t K, void *y, int out_dtype, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/*
+ * fp8_block_linear, fp8_block_linear_pow2 -- the whole FP8 linear layer from
+ * bf16 activations: Y = fp8_block_gemm(quant_act_1x128(X), Wq, Ws) (article
+ * section "Technical breakthrough": activations are quantized per 1x128
+ * block as they enter each linear layer).  The _pow2 form quantizes X with
+ * power-of-2 scales (FP8BS_SCALE_POW2) and runs fp8_block_gemm_pow2, whose
+ * precondition ws must then meet.
+ *
+ *   x [M, K] bf16 payloads, row-major
+ *   wq, ws, y, out_dtype: as fp8_block_gemm
+ *
+ * For at most 16 rows (decode) with 8 <= K/128 <= 128, one kernel reads x,
+ * quantizes each 1x128 block in registers with the quantizer's own encoder
+ * and multiplies, so no quantized copy of x is written or read back.  Other
+ * shapes run quant_act_1x128 into the workspace, then the GEMM.  Either way
+ * y is bit for bit that of quant_act_1x128 followed by fp8_block_gemm (or the
+ * _pow2 pair) on the same stream, with the default kernel selection (no
+ * FP8BS_GEMM_VARIANT override).
+ *
+ * Workspace: fp8bs_linear_workspace_size(M, N, K) bytes (0 for the fused
+ *   shapes, where workspace may be NULL): the quantized x, its scales, then
+ *   the GEMM's own workspace, each 16-byte aligned.  It need not be zeroed;
+ *   calls that share a workspace must not overlap in time.
+ * Errors: as fp8_block_gemm (x takes xq's place), plus UNSUPPORTED_SHAPE for
+ *   shapes quant_act_1x128 rejects.
+ */
+FP8BS_API int fp8_block_linear(const void *x_bf16, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+                               void *y, int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
+FP8BS_API int fp8_block_linear_pow2(const void *x_bf16, const void *wq, const float *ws, int64_t M, int64_t N,
+                                    int64_t K, void *y, int out_dtype, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* Workspace size in bytes for fp8_block_linear(_pow2) of this shape (0 for
+ * the fused decode shapes); no device call. */
+FP8BS_API size_t fp8bs_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
 /* Workspace sizes in bytes for the two GEMMs: functions of the shape (and of
  * the FP8BS_GEMM_VARIANT / FP8BS_GEMM_KSPLIT measurement overrides, read once
  * per process); no device call. */

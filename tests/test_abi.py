@@ -133,6 +133,35 @@ def test_gemm_validation(fp8bs):
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 256, FAKE, 0, NULL, 0, NULL) == 4   # no table space
 
 
+def test_linear_workspace_and_validation(fp8bs):
+    """fp8_block_linear: no workspace for the fused decode shapes (at most 16 rows, 8 <= K/128 <= 128);
+    elsewhere the quantized activations (codes, then fp32 scales, each 16-byte aligned) and the
+    GEMM's own workspace."""
+    L = fp8bs.lib()
+    wsz = L.fp8bs_linear_workspace_size
+    assert wsz(1, 28672, 4096) == 0 and wsz(16, 4096, 14336) == 0 and wsz(5, 128, 16384) == 0
+    assert wsz(0, 128, 128) == 0 and wsz(-1, 128, 1024) == 0
+
+    def a16(b):
+        return (b + 15) // 16 * 16
+    for M, N, K in ((17, 4096, 4096), (8192, 4096, 4096), (16, 256, 512), (3, 256, 32768), (64, 28672, 4096)):
+        assert wsz(M, N, K) == a16(M * K) + a16(M * (K // 128) * 4) + L.fp8bs_gemm_workspace_size(M, N, K)
+    for f in (L.fp8_block_linear, L.fp8_block_linear_pow2):
+        assert f(FAKE, FAKE, FAKE, 8, 100, 1024, FAKE, 0, NULL, 0, NULL) == 2     # N % 128
+        assert f(FAKE, FAKE, FAKE, 8, 128, 1000, FAKE, 0, NULL, 0, NULL) == 2    # K % 128
+        assert f(FAKE, FAKE, FAKE, -1, 128, 1024, FAKE, 0, NULL, 0, NULL) == 1   # M < 0
+        assert f(FAKE, FAKE, FAKE, 8, 128, 1024, FAKE, 3, NULL, 0, NULL) == 1    # out dtype
+        assert f(NULL, FAKE, FAKE, 8, 128, 1024, FAKE, 0, NULL, 0, NULL) == 1    # null activations
+        assert f(MISAL, FAKE, FAKE, 8, 128, 1024, FAKE, 0, NULL, 0, NULL) == 1   # misaligned activations
+        assert f(FAKE, FAKE, NULL, 8, 128, 1024, FAKE, 0, NULL, 0, NULL) == 1    # null weight scales
+        assert f(FAKE, FAKE, FAKE, 8, 128, 1024, MISAL, 0, NULL, 0, NULL) == 1   # misaligned output
+        assert f(NULL, FAKE, FAKE, 0, 128, 1024, NULL, 0, NULL, 0, NULL) == 0    # M == 0: no-op
+        need = wsz(17, 4096, 4096)
+        assert f(FAKE, FAKE, FAKE, 17, 4096, 4096, FAKE, 0, NULL, 0, NULL) == 4          # no workspace
+        assert f(FAKE, FAKE, FAKE, 17, 4096, 4096, FAKE, 0, FAKE, need - 1, NULL) == 4   # too small
+        assert f(FAKE, FAKE, FAKE, 17, 4096, 4096, FAKE, 0, MISAL, need, NULL) == 1      # misaligned
+
+
 def test_unsupported_device_without_gpu(fp8bs):
     """Valid arguments on a host with no HIP device: UNSUPPORTED_DEVICE, nothing launched."""
     import torch
