@@ -9,7 +9,10 @@ Workloads (--workload):
          down (K 14336, N 4096), o_proj (K 4096, N 4096).
   recal  per-step recalibration of 32 layers x 4 weights, EXACT then POW2.
   decode rollout decode: M in {1, 16, 64, 256} against the gate+up and down
-         weights, activations quantized on the fly.
+         weights, through fp8_block_linear from bf16 activations (one launch
+         that quantizes inside the GEMM for M <= 16 where the W tiles are 32 or
+         64 rows, i.e. gate+up); the separate quantizer and GEMM calls are
+         timed after the step for comparison.
   moe    MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens
          routed top-8: expert-weight recalibration, quantization of the
          gate+up and down inputs, the two grouped GEMMs.
@@ -275,7 +278,7 @@ def cpu_baseline_recal(target_s=12.0):
 def decode_workload(fp8bs, dev, mode):
     # POW2 scales go to the entry points that apply them through the matrix cores
     gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
-    grouped = fp8bs.fp8_block_grouped_gemm_pow2 if mode else fp8bs.fp8_block_grouped_gemm
+    linear = fp8bs.fp8_block_linear_pow2 if mode else fp8bs.fp8_block_linear
     import synth
     import torch
     pairs = []
@@ -294,21 +297,33 @@ def decode_workload(fp8bs, dev, mode):
                               xs=torch.empty((M, K // 128), dtype=torch.float32, device=dev),
                               y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                               ws_buf=torch.empty(max(1, fp8bs.gemm_workspace_size(M, N, K)), dtype=torch.uint8,
-                                                 device=dev)))
+                                                 device=dev),
+                              lin_buf=torch.empty(max(1, fp8bs.linear_workspace_size(M, N, K)), dtype=torch.uint8,
+                                                  device=dev)))
     it = [0]
 
     def step(timer):
+        # the linear layer from bf16 activations: one launch for M <= 16 (X
+        # quantized inside the weight-streaming GEMM), quantizer + GEMM above
         c = it[0] % 5
         it[0] += 1
         for p in pairs:
             wq, ws = p["copies"][c]
-            maybe(timer, "quant_" + p["name"], lambda p=p: fp8bs.quant_act_1x128(p["x"], mode, out=(p["xq"], p["xs"])))
-            maybe(timer, "gemm_" + p["name"],
-                  lambda p=p, wq=wq, ws=ws: gemm(p["xq"], p["xs"], wq, ws, out=p["y"],
-                                                                 workspace=p["ws_buf"]))
+            maybe(timer, "linear_" + p["name"],
+                  lambda p=p, wq=wq, ws=ws: linear(p["x"], wq, ws, out=p["y"], workspace=p["lin_buf"]))
+
+    def separate(timer, reps):
+        # the same layer as two separate calls, timed apart (reported beside the step)
+        for r in range(reps):
+            for p in pairs:
+                wq, ws = p["copies"][r % 5]
+                maybe(timer, "quant_" + p["name"],
+                      lambda p=p: fp8bs.quant_act_1x128(p["x"], mode, out=(p["xq"], p["xs"])))
+                maybe(timer, "gemm_" + p["name"],
+                      lambda p=p, wq=wq, ws=ws: gemm(p["xq"], p["xs"], wq, ws, out=p["y"], workspace=p["ws_buf"]))
 
     flops = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pairs)
-    return step, pairs, flops
+    return step, separate, pairs, flops
 
 
 def moe_workload(fp8bs, dev, mode):
@@ -478,17 +493,25 @@ def main():
                "kernels": {"recal_exact": hbm_entry(te, nbytes), "recal_pow2": hbm_entry(tp, nbytes)}}
         cpu = (lambda: cpu_baseline_recal()) if not args.no_cpu_baseline else None
     elif args.workload == "decode":
-        step, pairs, flops = decode_workload(fp8bs, dev, args.mode)
+        step, separate, pairs, flops = decode_workload(fp8bs, dev, args.mode)
         ms = timed_loop(step, args.steps, args.warmup, timer)
+        separate(None, 2)
+        separate(timer, args.steps)
+        torch.cuda.synchronize()
         kernels = {}
         for p in pairs:
+            tl = timer.avg_ms("linear_" + p["name"])
             tg = timer.avg_ms("gemm_" + p["name"])
             tq = timer.avg_ms("quant_" + p["name"])
-            # GEMM alone: Wq + Ws + Xq + Xs + Y; quantize + GEMM adds the bf16 read of X
-            gbytes = p["N"] * p["K"] * (1 + 4 / 16384) + p["M"] * p["K"] * (1 + 4 / 128) + p["M"] * p["N"] * 2
-            kernels["gemm_" + p["name"]] = {**hbm_entry(tg, gbytes),
-                                            "TFLOP/s": round(2.0 * p["M"] * p["N"] * p["K"] / (tg * 1e-3) / 1e12, 2)}
+            # GEMM alone: Wq + Ws + Xq + Xs + Y; the linear layer reads bf16 X instead of Xq + Xs
+            wb = p["N"] * p["K"] * (1 + 4 / 16384) + p["M"] * p["N"] * 2
+            gbytes = wb + p["M"] * p["K"] * (1 + 4 / 128)
+            tf = lambda t, p=p: round(2.0 * p["M"] * p["N"] * p["K"] / (t * 1e-3) / 1e12, 2)
+            kernels["linear_" + p["name"]] = {**hbm_entry(tl, wb + p["M"] * p["K"] * 2), "TFLOP/s": tf(tl),
+                                              "fused": fp8bs.linear_workspace_size(p["M"], p["N"], p["K"]) == 0}
+            kernels["gemm_" + p["name"]] = {**hbm_entry(tg, gbytes), "TFLOP/s": tf(tg)}
             kernels["quant_plus_gemm_" + p["name"]] = hbm_entry(tq + tg, gbytes + p["M"] * p["K"] * 2)
+        # the step's longest single GEMM launch: the largest M (persistent kernel split along K)
         big = max(pairs, key=lambda p: p["N"] * p["K"] + p["M"])
         tb = timer.avg_ms("gemm_" + big["name"])
         nb = big["N"] * big["K"] * (1 + 4 / 16384) + big["M"] * big["K"] * (1 + 4 / 128) + big["M"] * big["N"] * 2
@@ -496,8 +519,10 @@ def main():
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", **common,
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "rollout decode: M in {1,16,64,256} x (gate+up K4096 N28672, down K14336 "
-                                      "N4096), activations quantized on the fly, 5 rotated weight copies"},
-               "roofline": {"kernel": "fp8_block_gemm (weight-streaming kernel), %s" % big["name"], "bound": "hbm",
+                                      "N4096), fp8_block_linear from bf16 activations (quantized inside the GEMM "
+                                      "for M <= 16), 5 rotated weight copies"},
+               "roofline": {"kernel": "fp8_block_gemm (persistent 128x256 kernel split along K), %s" % big["name"],
+                            "bound": "hbm",
                             "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None},
                "kernels": kernels}

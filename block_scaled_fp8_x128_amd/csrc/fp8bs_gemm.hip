@@ -1348,16 +1348,15 @@ static hipError_t run_skinny_t(GemmArgs a, bool out_f32, hipStream_t stream)
 }
 
 // The weight-streaming kernel on bf16 activations (M <= 16: one 16-row X
-// tile), quantizing them itself with EXACT (QX = 1) or POW2 (QX = 2) scales.
+// tile), quantizing them itself with EXACT (QX = 1) or POW2 (QX = 2) scales,
+// with the 64- or 32-row W tiles the plain kernel would pick (linear_fused
+// admits no other shape).
 template <int QX>
 static hipError_t run_skinny_qx(GemmArgs a, bool out_f32, hipStream_t stream)
 {
-    const int64_t N = a.N;
-    if (N % 64 == 0 && N / 64 >= 256)
+    if (a.N % 64 == 0 && a.N / 64 >= 256)
         return run_skinny_t<1, 4, 4, QX>(a, out_f32, stream);
-    if (N % 32 == 0 && N / 32 >= 256)
-        return run_skinny_t<1, 2, 4, QX>(a, out_f32, stream);
-    return run_skinny_t<1, 1, 6, QX>(a, out_f32, stream);
+    return run_skinny_t<1, 2, 4, QX>(a, out_f32, stream);
 }
 
 // W tile width: the widest of 64 / 32 / 16 rows that still gives at least 256
@@ -1491,11 +1490,17 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
 // ---- the whole linear layer: bf16 activations in ---------------------------------
 //
 // Y = fp8_block_gemm(quant_act_1x128(X), Wq, Ws).  Decode shapes (at most 16
-// rows, on shapes the weight-streaming kernel takes) run as one launch that
-// quantizes X inside the GEMM; every other shape quantizes X into the
-// workspace and runs the GEMM on it.  Either way the codes, scales and Y are
-// those of the two separate calls.
-static bool linear_fused(int64_t M, int64_t N, int64_t K) { return M <= kSkinnyMaxM && skinny_ok(M, N, K); }
+// rows, on shapes the weight-streaming kernel takes with W tiles of 32 or 64
+// rows) run as one launch that quantizes X inside the GEMM; every other shape
+// quantizes X into the workspace and runs the GEMM on it.  Either way the
+// codes, scales and Y are those of the two separate calls.  (With 16-row W
+// tiles the plain kernel fits two workgroups per CU and the fused one, holding
+// bf16 X in flight, only one: the two calls were faster there, e.g. 25 us
+// against 33 us for 1 x 14336 x 4096.)
+static bool linear_fused(int64_t M, int64_t N, int64_t K)
+{
+    return M <= kSkinnyMaxM && skinny_ok(M, N, K) && N % 32 == 0 && N / 32 >= 256;
+}
 
 static size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
 

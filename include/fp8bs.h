@@ -221,10 +221,11 @@ FP8BS_API int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const
  *   x [M, K] bf16 payloads, row-major
  *   wq, ws, y, out_dtype: as fp8_block_gemm
  *
- * For at most 16 rows (decode) with 8 <= K/128 <= 128, one kernel reads x,
- * quantizes each 1x128 block in registers with the quantizer's own encoder
- * and multiplies, so no quantized copy of x is written or read back.  Other
- * shapes run quant_act_1x128 into the workspace, then the GEMM.  Either way
+ * For at most 16 rows (decode) with 8 <= K/128 <= 128 and N a multiple of 32
+ * with N/32 >= 256, one kernel reads x, quantizes each 1x128 block in
+ * registers with the quantizer's own encoder and multiplies, so no quantized
+ * copy of x is written or read back.  Other shapes run quant_act_1x128 into
+ * the workspace, then the GEMM.  Either way
  * y is bit for bit that of quant_act_1x128 followed by fp8_block_gemm (or the
  * _pow2 pair) on the same stream, with the default kernel selection (no
  * FP8BS_GEMM_VARIANT override).

@@ -134,17 +134,18 @@ def test_gemm_validation(fp8bs):
 
 
 def test_linear_workspace_and_validation(fp8bs):
-    """fp8_block_linear: no workspace for the fused decode shapes (at most 16 rows, 8 <= K/128 <= 128);
-    elsewhere the quantized activations (codes, then fp32 scales, each 16-byte aligned) and the
-    GEMM's own workspace."""
+    """fp8_block_linear: no workspace for the fused decode shapes (at most 16 rows, 8 <= K/128 <= 128,
+    N a multiple of 32 with N/32 >= 256); elsewhere the quantized activations (codes, then fp32
+    scales, each 16-byte aligned) and the GEMM's own workspace."""
     L = fp8bs.lib()
     wsz = L.fp8bs_linear_workspace_size
-    assert wsz(1, 28672, 4096) == 0 and wsz(16, 4096, 14336) == 0 and wsz(5, 128, 16384) == 0
+    assert wsz(1, 28672, 4096) == 0 and wsz(16, 8192, 1024) == 0 and wsz(5, 16384, 16384) == 0
     assert wsz(0, 128, 128) == 0 and wsz(-1, 128, 1024) == 0
 
     def a16(b):
         return (b + 15) // 16 * 16
-    for M, N, K in ((17, 4096, 4096), (8192, 4096, 4096), (16, 256, 512), (3, 256, 32768), (64, 28672, 4096)):
+    for M, N, K in ((17, 4096, 4096), (8192, 4096, 4096), (16, 256, 512), (3, 256, 32768), (64, 28672, 4096),
+                    (16, 4096, 14336), (1, 8064, 4096), (2, 8192, 896), (1, 8192, 16512)):
         assert wsz(M, N, K) == a16(M * K) + a16(M * (K // 128) * 4) + L.fp8bs_gemm_workspace_size(M, N, K)
     for f in (L.fp8_block_linear, L.fp8_block_linear_pow2):
         assert f(FAKE, FAKE, FAKE, 8, 100, 1024, FAKE, 0, NULL, 0, NULL) == 2     # N % 128
