@@ -13,6 +13,9 @@ Workloads (--workload):
          that quantizes inside the GEMM for M <= 16 where the W tiles are 32 or
          64 rows, i.e. gate+up); the separate quantizer and GEMM calls are
          timed after the step for comparison.
+  train  training backward of the dense layer: W and W^T codes from one
+         batched recalibration launch, quantization of the four output
+         gradients dY, and the four data-gradient GEMMs dX = dY W.
   moe    MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens
          routed top-8: expert-weight recalibration, quantization of the
          gate+up and down inputs, the two grouped GEMMs.
@@ -183,7 +186,44 @@ def dense_workload(fp8bs, dev, mode):
     return step, bufs, flops
 
 
-def summarize_dense(bufs, timer):
+def train_workload(fp8bs, dev, mode):
+    """Backward data gradients of the same four layers: dX [M, K] = dY [M, N] W [N, K]."""
+    gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
+    import synth
+    import torch
+    M = 8192
+    bufs = []
+    for i, (name, N, K) in enumerate(DENSE):
+        log("generating %s: dY [%d, %d], W [%d, %d]" % (name, M, N, N, K))
+        dy = bf16_dev(synth.activations(M, N, sub=synth.SUB_DY + 10 * i), dev)
+        w = bf16_dev(synth.weights(N, K, sub=synth.sub_layer(i)), dev)
+        outs = (torch.empty((N, K), dtype=torch.uint8, device=dev),
+                torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
+                torch.empty((K, N), dtype=torch.uint8, device=dev),
+                torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev))
+        dyq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        dys = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        # the GEMM runs with the forward (N, K) swapped: output width K, reduction over N
+        bufs.append(dict(name=name, M=M, N=K, K=N, dy=dy, w=w, outs=outs, dyq=dyq, dys=dys, dx=dx))
+
+    w_all = [b["w"] for b in bufs]
+    out_all = [b["outs"] for b in bufs]
+
+    def step(timer):
+        # the step's recalibration for training: W and W^T codes from one read of each weight
+        maybe(timer, "quant_w_all", lambda: fp8bs.quant_w_128x128_dual_batched(w_all, mode, outs=out_all))
+        for b in bufs:
+            maybe(timer, "quant_act_" + b["name"],
+                  lambda: fp8bs.quant_act_1x128(b["dy"], mode, out=(b["dyq"], b["dys"])))
+            maybe(timer, "gemm_" + b["name"],
+                  lambda: gemm(b["dyq"], b["dys"], b["outs"][2], b["outs"][3], out=b["dx"]))
+
+    flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
+    return step, bufs, flops
+
+
+def summarize_dense(bufs, timer, dual=False):
     kernels = {}
     gemm_ms, gemm_flops = [], []
     for b in bufs:
@@ -194,15 +234,19 @@ def summarize_dense(bufs, timer):
         gemm_flops.append(2.0 * M * N * K)
         kernels["quant_act_" + b["name"]] = hbm_entry(timer.avg_ms("quant_act_" + b["name"]),
                                                       M * K * 3 + (M * K // 128) * 4)
+    # bf16 read, codes written (twice for the dual form: W and W^T), one fp32 per block (twice)
+    wb = 4 if dual else 3
     kernels["quant_w_all"] = hbm_entry(timer.avg_ms("quant_w_all"),
-                                       sum(b["N"] * b["K"] * 3 + (b["N"] * b["K"] // 16384) * 4 for b in bufs))
+                                       sum(b["N"] * b["K"] * wb + (b["N"] * b["K"] // 16384) * 4 * (wb - 2)
+                                           for b in bufs))
     # The four GEMMs run one kernel (the 256 x 256 persistent block-scaled
     # GEMM): per launch, mean algorithmic FLOP / mean duration.
     mean_ms = sum(gemm_ms) / len(gemm_ms)
     mean_flops = sum(gemm_flops) / len(gemm_flops)
     ach = mean_flops / (mean_ms * 1e-3) / 1e12
     traffic, tsrc = traffic_for("dense")
-    roof = {"kernel": DOMINANT["dense"][0] + " (QKV, gate+up, down, o_proj at M=8192)", "bound": "mfma",
+    what = "data gradients of " if dual else ""
+    roof = {"kernel": DOMINANT["dense"][0] + " (%sQKV, gate+up, down, o_proj at M=8192)" % what, "bound": "mfma",
             "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
             "algorithmic_flop_per_launch": mean_flops, "avg_launch_ms": round(mean_ms, 4),
@@ -437,7 +481,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "recal", "decode", "moe"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "recal", "decode", "moe", "train"])
     ap.add_argument("--mode", type=int, default=0, help="scale mode: 0 EXACT, 1 POW2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -448,7 +492,7 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(every kernel runs on one GPU's share at its real shape); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
@@ -476,6 +520,20 @@ def main():
                           "gemm_flops_per_step": flops},
                "roofline": roof, "kernels": kernels}
         cpu = (lambda: cpu_baseline_dense()) if not args.no_cpu_baseline else None
+    elif args.workload == "train":
+        step, bufs, flops = train_workload(fp8bs, dev, args.mode)
+        ms = timed_loop(step, args.steps, args.warmup, timer)
+        kernels, roof = summarize_dense(bufs, timer, dual=True)
+        out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
+               "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
+               "config": {"workload": "training backward of the 8B-shaped dense layer at M=8192 tokens: "
+                                      "recalibrate 4 weights to W and W^T codes (one batched launch), quantize "
+                                      "4 output gradients dY (1x128 along N), data-gradient GEMMs dX = dY W for "
+                                      "QKV, gate+up, down, o_proj",
+                          "scale_mode": "pow2" if args.mode else "exact", "out_dtype": "bf16",
+                          "gemm_flops_per_step": flops},
+               "roofline": roof, "kernels": kernels}
+        cpu = None
     elif args.workload == "recal":
         step, nbytes = recal_workload(fp8bs, dev)
         ms = timed_loop(step, args.steps, args.warmup, timer)

@@ -35,6 +35,8 @@ EXPORTS = (
     "quant_act_1x128",
     "quant_w_128x128",
     "quant_w_128x128_batched",
+    "quant_w_128x128_dual",
+    "quant_w_128x128_dual_batched",
     "fp8_block_gemm",
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_pow2",
@@ -68,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.quant_act_1x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
+        L.quant_w_128x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
+        L.quant_w_128x128_dual_batched.argtypes = [I64, P, P, P, P, P, P, P, I32, P]
         L.fp8_block_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_gemm_pow2.argtypes = L.fp8_block_gemm.argtypes
@@ -83,7 +87,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.argtypes = [I32]
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
-        for fn in ("quant_act_1x128", "quant_w_128x128", "quant_w_128x128_batched", "fp8_block_gemm",
+        for fn in ("quant_act_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
+                   "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
             getattr(L, fn).restype = I32
@@ -189,6 +194,48 @@ def quant_w_128x128_batched(ws_in: Sequence[torch.Tensor], mode: int = SCALE_EXA
                                        ctypes.cast(Ks, ctypes.c_void_p), ctypes.cast(qp, ctypes.c_void_p),
                                        ctypes.cast(sp, ctypes.c_void_p), int(mode), _stream(tensors[0]))
     _check("quant_w_128x128_batched", st)
+    return outs
+
+
+def _dual_outs(w: torch.Tensor):
+    N, K = w.shape
+    return (torch.empty((N, K), dtype=torch.uint8, device=w.device),
+            torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device),
+            torch.empty((K, N), dtype=torch.uint8, device=w.device),
+            torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device))
+
+
+def quant_w_128x128_dual(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 [N, K] -> (wq [N, K], ws [N/128, K/128], wqt [K, N], wst [K/128, N/128]):
+    the codes and scales of W and of W^T from one read of W."""
+    w = _bf16_payload(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    wq, ws, wqt, wst = out if out is not None else _dual_outs(w)
+    _check("quant_w_128x128_dual", lib().quant_w_128x128_dual(_ptr(w), N, K, _ptr(wq), _ptr(ws), _ptr(wqt),
+                                                              _ptr(wst), int(mode), _stream(w)))
+    return wq, ws, wqt, wst
+
+
+def quant_w_128x128_dual_batched(ws_in: Sequence[torch.Tensor], mode: int = SCALE_EXACT, outs=None):
+    """quant_w_128x128_dual over many weight tensors in one call."""
+    n = len(ws_in)
+    if n == 0:
+        return []
+    tensors = [_bf16_payload(w, "w[%d]" % i) for i, w in enumerate(ws_in)]
+    if outs is None:
+        outs = [_dual_outs(w) for w in tensors]
+    arr_p = ctypes.c_void_p * n
+    arr_i = ctypes.c_int64 * n
+    cols = [arr_p(*[o[j].data_ptr() for o in outs]) for j in range(4)]
+    wp = arr_p(*[w.data_ptr() for w in tensors])
+    Ns = arr_i(*[w.shape[0] for w in tensors])
+    Ks = arr_i(*[w.shape[1] for w in tensors])
+    cv = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+    st = lib().quant_w_128x128_dual_batched(n, cv(wp), cv(Ns), cv(Ks), *[cv(c) for c in cols], int(mode),
+                                            _stream(tensors[0]))
+    _check("quant_w_128x128_dual_batched", st)
     return outs
 
 

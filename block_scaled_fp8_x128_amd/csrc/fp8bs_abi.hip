@@ -178,6 +178,61 @@ int quant_w_128x128_batched(int64_t count, const void *const *w_bf16, const int6
     return FP8BS_OK;
 }
 
+static int quant_w_dual_impl(int64_t count, const void *const *w_bf16, const int64_t *N, const int64_t *K,
+                             void *const *wq, float *const *ws, void *const *wqt, float *const *wst, int scale_mode,
+                             void *stream)
+{
+    if (count < 0)
+        return FP8BS_INVALID_ARG;
+    if (count == 0)
+        return FP8BS_OK;
+    if (!w_bf16 || !N || !K || !wq || !ws || !wqt || !wst)
+        return FP8BS_INVALID_ARG;
+    bool any = false;
+    for (int64_t i = 0; i < count; ++i) {
+        int st = check_quant(w_bf16[i], N[i], K[i], wq[i], ws[i], scale_mode, true);
+        if (st != FP8BS_OK)
+            return st;
+        // the transposed outputs: codes [K, N] and scales [K/128, N/128]
+        if (!tensor_ok(wqt[i], N[i] * K[i], 16) || !tensor_ok(wst[i], N[i] * K[i], 4))
+            return FP8BS_INVALID_ARG;
+        any = any || N[i] > 0;
+    }
+    if (!any)
+        return FP8BS_OK;
+    int st = check_device();
+    if (st != FP8BS_OK)
+        return st;
+    fp8bs::WTensor buf[64];
+    int64_t n = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        if (N[i] == 0)
+            continue;
+        buf[n++] = fp8bs::WTensor{w_bf16[i], wq[i], ws[i], N[i], K[i], wqt[i], wst[i]};
+        if (n == 64) {
+            if (fp8bs::launch_quant_w_dual(buf, n, scale_mode, (hipStream_t)stream) != hipSuccess)
+                return FP8BS_HIP_ERROR;
+            n = 0;
+        }
+    }
+    if (n > 0 && fp8bs::launch_quant_w_dual(buf, n, scale_mode, (hipStream_t)stream) != hipSuccess)
+        return FP8BS_HIP_ERROR;
+    return FP8BS_OK;
+}
+
+int quant_w_128x128_dual(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, void *wqt, float *wst,
+                         int scale_mode, void *stream)
+{
+    return quant_w_dual_impl(1, &w_bf16, &N, &K, &wq, &ws, &wqt, &wst, scale_mode, stream);
+}
+
+int quant_w_128x128_dual_batched(int64_t count, const void *const *w_bf16, const int64_t *N, const int64_t *K,
+                                 void *const *wq, float *const *ws, void *const *wqt, float *const *wst,
+                                 int scale_mode, void *stream)
+{
+    return quant_w_dual_impl(count, w_bf16, N, K, wq, ws, wqt, wst, scale_mode, stream);
+}
+
 size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K <= 0)

@@ -31,16 +31,21 @@ static inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, s
 
 hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float *xs, int mode, hipStream_t stream);
 
-// One weight tensor of a batched weight quantization.
+// One weight tensor of a batched weight quantization (qt, st: the transposed
+// codes [K, N] and scales [K/128, N/128], written by the dual launcher only).
 struct WTensor {
     const void *w;
     void *q;
     float *s;
     int64_t N, K;
+    void *qt = nullptr;
+    float *st = nullptr;
 };
 // Quantizes `count` tensors (count >= 1, every N, K a positive multiple of
 // 128) in as few launches as the kernel-argument budget allows.
 hipError_t launch_quant_w(const WTensor *t, int64_t count, int mode, hipStream_t stream);
+// The same, also writing each tensor's transposed codes and scales (qt, st).
+hipError_t launch_quant_w_dual(const WTensor *t, int64_t count, int mode, hipStream_t stream);
 
 // ---- GEMMs (fp8bs_gemm.hip) --------------------------------------------------
 

@@ -186,4 +186,179 @@ hipError_t launch_quant_w(const WTensor *t, int64_t count, int mode, hipStream_t
     return hipSuccess;
 }
 
+// ---- weights for training: codes of W and of its transpose in one pass ----------
+//
+// The backward pass multiplies by W^T (dX = dY W), whose 128x128 blocks are
+// those of W transposed: block (kb, nb) of W^T holds the same 16384 values as
+// block (nb, kb) of W, so its amax, scale and codes are the same, moved.  One
+// read of the bf16 block therefore yields both operand sets, 4 bytes of
+// traffic per element against 6 for two separate passes.  The workgroup
+// loads the block as quant_w_kernel does, except that thread t covers 16-byte
+// chunk (t % 16) of the 8 consecutive rows 8 (t / 16) .. + 7 -- an 8x8 byte
+// square of codes, which it transposes in registers (byte permutes) into 8
+// row pieces of the transposed block, each 8 contiguous bytes, gathered into
+// whole rows through LDS.
+struct QWDArgs {
+    int count;
+    int64_t tile_begin[QW_MAX_TENSORS + 1];
+    const uint16_t *w[QW_MAX_TENSORS];
+    uint8_t *q[QW_MAX_TENSORS];
+    float *s[QW_MAX_TENSORS];
+    uint8_t *qt[QW_MAX_TENSORS];
+    float *st[QW_MAX_TENSORS];
+    int64_t N[QW_MAX_TENSORS];
+    int64_t K[QW_MAX_TENSORS];
+};
+
+// Transpose of an 8x8 byte square: row j is (lo[j], hi[j]) (bytes 0-3, 4-7);
+// on return row i of the result holds byte i of every input row.
+__device__ __forceinline__ void transpose8x8(const uint32_t (&lo)[8], const uint32_t (&hi)[8], uint32_t (&olo)[8],
+                                             uint32_t (&ohi)[8])
+{
+    // 4x4 byte squares: (rows 0-3 | 4-7) x (bytes 0-3 | 4-7).  Within a square
+    // first interleave the bytes of row pairs, then the halves of the pairs.
+    // __builtin_amdgcn_perm(a, b, sel): byte k of the result is byte sel_k of
+    // the 8-byte value a:b (0-3 from b, 4-7 from a).
+    auto square = [](uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t &c0, uint32_t &c1, uint32_t &c2,
+                     uint32_t &c3) {
+        const uint32_t a_lo = __builtin_amdgcn_perm(r1, r0, 0x05010400u); // r0.b0 r1.b0 r0.b1 r1.b1
+        const uint32_t a_hi = __builtin_amdgcn_perm(r1, r0, 0x07030602u); // r0.b2 r1.b2 r0.b3 r1.b3
+        const uint32_t b_lo = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+        const uint32_t b_hi = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+        c0 = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u); // r0.b0 r1.b0 r2.b0 r3.b0
+        c1 = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
+        c2 = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
+        c3 = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+    };
+    // output row i < 4 takes byte i of lo[j]; i >= 4 byte i - 4 of hi[j];
+    // its bytes 0-3 come from input rows 0-3, bytes 4-7 from rows 4-7
+    square(lo[0], lo[1], lo[2], lo[3], olo[0], olo[1], olo[2], olo[3]);
+    square(lo[4], lo[5], lo[6], lo[7], ohi[0], ohi[1], ohi[2], ohi[3]);
+    square(hi[0], hi[1], hi[2], hi[3], olo[4], olo[5], olo[6], olo[7]);
+    square(hi[4], hi[5], hi[6], hi[7], ohi[4], ohi[5], ohi[6], ohi[7]);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(QW_THREADS) void quant_w_dual_kernel(QWDArgs a)
+{
+    __shared__ uint32_t red[QW_THREADS / 64];
+    __shared__ __attribute__((aligned(16))) uint8_t tl[128 * 128]; // the transposed code block
+    const int64_t tile = blockIdx.x;
+    int i = 0;
+    while (i + 1 < a.count && tile >= a.tile_begin[i + 1])
+        ++i;
+    const int64_t N = a.N[i], K = a.K[i];
+    const int64_t KB = K / 128, NB = N / 128;
+    const int64_t local = tile - a.tile_begin[i];
+    const int64_t nb = local / KB, kb = local % KB;
+
+    const int t = threadIdx.x;
+    const int rg = t >> 4, c = t & 15; // rows 8 rg .. 8 rg + 7, columns 8 c .. 8 c + 7 of the block
+    const int64_t base = (nb * 128 + 8 * rg) * K + kb * 128 + c * 8;
+    const uint16_t *w = a.w[i];
+
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = __builtin_nontemporal_load((const u32x4 *)(w + base + j * K));
+
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t cm = chunk_max_mag(v[j]);
+        m = m > cm ? m : cm;
+    }
+    m = row16_max(m);
+    {
+        const uint32_t a0 = __builtin_amdgcn_readlane(m, 0), a1 = __builtin_amdgcn_readlane(m, 16);
+        const uint32_t a2 = __builtin_amdgcn_readlane(m, 32), a3 = __builtin_amdgcn_readlane(m, 48);
+        uint32_t wm = a0 > a1 ? a0 : a1;
+        const uint32_t wm2 = a2 > a3 ? a2 : a3;
+        wm = wm > wm2 ? wm : wm2;
+        if ((t & 63) == 0)
+            red[t >> 6] = wm;
+    }
+    __syncthreads();
+    uint32_t bm = red[0];
+#pragma unroll
+    for (int j = 1; j < QW_THREADS / 64; ++j)
+        bm = bm > red[j] ? bm : red[j];
+
+    BlockQuant<MODE> bq;
+    bq.init(amax_value(bm));
+    uint8_t *q = a.q[i];
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const u32x2 codes = quant_chunk<MODE>(v[j], bq);
+        __builtin_nontemporal_store(codes, (u32x2 *)(q + base + j * K));
+        lo[j] = codes.x;
+        hi[j] = codes.y;
+    }
+    // transposed block (kb, nb) of W^T [K, N]: its row 8 c + r holds column
+    // 8 c + r of this block, whose bytes 8 rg .. 8 rg + 7 this thread holds.
+    // The 16 KiB block is assembled in LDS so that each store instruction
+    // writes whole 128-byte rows (stored straight from the 8x8 squares, a
+    // wave instruction wrote 16 scattered 32-byte pieces and the kernel ran
+    // at a third of the bandwidth).  LDS row p holds transposed row p, its
+    // 8-byte piece g at slot g ^ (p / 8): the 16 lanes of a write that share
+    // a piece index then fall in different banks.
+    uint32_t tlo[8], thi[8];
+    transpose8x8(lo, hi, tlo, thi);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        *(u32x2 *)(tl + (8 * c + r) * 128 + ((rg ^ c) << 3)) = u32x2{tlo[r], thi[r]};
+    __syncthreads();
+    uint8_t *qt = a.qt[i];
+    const int64_t tbase = kb * 128 * N + nb * 128;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        // 16-byte piece cc of transposed row tr, i.e. logical pieces 2 cc and
+        // 2 cc + 1, stored at slots (2 cc) ^ g and (2 cc + 1) ^ g (g = tr / 8):
+        // one aligned pair, in reverse order when g is odd
+        const int idx = p * QW_THREADS + t;
+        const int tr = idx >> 3, cc = idx & 7, g = tr >> 3;
+        u32x4 d = *(const u32x4 *)(tl + tr * 128 + ((((2 * cc) ^ g) >> 1) << 4));
+        if (g & 1)
+            d = u32x4{d.z, d.w, d.x, d.y};
+        __builtin_nontemporal_store(d, (u32x4 *)(qt + tbase + tr * N + cc * 16));
+    }
+    if (t == 0) {
+        a.s[i][nb * KB + kb] = bq.s;
+        a.st[i][kb * NB + nb] = bq.s;
+    }
+}
+
+hipError_t launch_quant_w_dual(const WTensor *t, int64_t count, int mode, hipStream_t stream)
+{
+    for (int64_t first = 0; first < count; first += QW_MAX_TENSORS) {
+        QWDArgs a = {};
+        const int64_t n = (count - first) < QW_MAX_TENSORS ? (count - first) : QW_MAX_TENSORS;
+        int64_t tiles = 0;
+        for (int64_t j = 0; j < n; ++j) {
+            const WTensor &wt = t[first + j];
+            a.tile_begin[j] = tiles;
+            a.w[j] = (const uint16_t *)wt.w;
+            a.q[j] = (uint8_t *)wt.q;
+            a.s[j] = wt.s;
+            a.qt[j] = (uint8_t *)wt.qt;
+            a.st[j] = wt.st;
+            a.N[j] = wt.N;
+            a.K[j] = wt.K;
+            tiles += (wt.N / 128) * (wt.K / 128);
+        }
+        a.tile_begin[n] = tiles;
+        a.count = (int)n;
+        if (tiles == 0)
+            continue;
+        hipError_t e = (mode == SCALE_POW2) ? launch(quant_w_dual_kernel<SCALE_POW2>, dim3((unsigned)tiles),
+                                                     dim3(QW_THREADS), 0, stream, a)
+                                            : launch(quant_w_dual_kernel<SCALE_EXACT>, dim3((unsigned)tiles),
+                                                     dim3(QW_THREADS), 0, stream, a);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
 } // namespace fp8bs

@@ -126,6 +126,40 @@ FP8BS_API int quant_w_128x128_batched(int64_t count, const void *const *w_bf16, 
                             void *stream);
 
 /*
+ * quant_w_128x128_dual -- the weight quantizer for training: the codes and
+ * scales of W and, from the same read of W, those of its transpose.  The
+ * article's recipe runs FP8 in training as well as in generation (section
+ * "Technical breakthrough"); the backward product dX = dY W multiplies by
+ * W^T, whose 128x128 blocks are W's blocks transposed, so block (kb, nb) of
+ * W^T has the amax, scale and codes of block (nb, kb) of W, moved.
+ *
+ *   w_bf16 : [N, K] bf16 payloads (input)
+ *   wq, ws : exactly as quant_w_128x128 writes them ([N, K], [N/128, K/128])
+ *   wqt    : [K, N] E4M3 codes, wqt[k, n] = wq[n, k]
+ *   wst    : [K/128, N/128] fp32 scales, wst[kb, nb] = ws[nb, kb]
+ * so (wqt, wst) equals quant_w_128x128 of the transposed matrix, and
+ * fp8_block_gemm(dyq, dys, wqt, wst, M, K, N) is the data gradient for
+ * dY [M, N] quantized by quant_act_1x128.  All outputs are caller-owned
+ * device buffers; wqt and wq are 16-byte aligned, the scales 4-byte aligned.
+ * Errors: as quant_w_128x128, and INVALID_ARG for a null or misaligned
+ * transposed output.
+ */
+FP8BS_API int quant_w_128x128_dual(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, void *wqt,
+                                   float *wst, int scale_mode, void *stream);
+
+/*
+ * quant_w_128x128_dual_batched -- quant_w_128x128_dual over `count` tensors
+ * in one launch (per-step recalibration of a model's weights for training).
+ * The seven arrays are HOST arrays of `count` entries, read during the call
+ * only; the pointers they hold are device pointers.  Errors: as
+ * quant_w_128x128_dual for any tensor; INVALID_ARG if count < 0 or an array
+ * is null with count > 0.  count == 0 is a no-op.
+ */
+FP8BS_API int quant_w_128x128_dual_batched(int64_t count, const void *const *w_bf16, const int64_t *N,
+                                           const int64_t *K, void *const *wq, float *const *ws,
+                                           void *const *wqt, float *const *wst, int scale_mode, void *stream);
+
+/*
  * fp8_block_gemm -- Y = dequant(Xq) * dequant(Wq)^T, the FP8 linear layer
  * (article section "Technical breakthrough": linear layers run FP8 math).
  *

@@ -13,6 +13,9 @@ values are synthetic):
 * activations: fp32 N(0, 1); each entry independently, with probability 1e-3,
   is multiplied by 50 (outliers); then rounded to bf16 (round to nearest even);
 * weights: fp32 0.02 * N(0, 1), rounded to bf16;
+* output gradients dY (training backward): the activation recipe, from
+  their own sub-stream (the article prints no gradient statistics; block
+  scaling makes every result invariant to a common power-of-2 factor);
 * MoE router: fp32 N(0, 1) logits [tokens, experts]; each token goes to its
   top-k experts by logit (softmax is monotone, so this is top-k by
   probability), ties to the lower expert id; rows are grouped by expert, then
@@ -31,6 +34,7 @@ SEED = 0
 SUB_X = 0
 SUB_W = 1
 SUB_ROUTER = 2
+SUB_DY = 3      # output gradients of the backward (data-gradient) product
 
 
 def sub_layer(layer: int) -> int:

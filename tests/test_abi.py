@@ -109,6 +109,28 @@ def test_quant_w_validation(fp8bs):
     assert b(2, arr, Ns, Ks, arr, arr, 0, NULL) == 2      # second tensor N % 128
 
 
+def test_quant_w_dual_validation(fp8bs):
+    L = fp8bs.lib()
+    q = L.quant_w_128x128_dual
+    assert q(FAKE, 100, 128, FAKE, FAKE, FAKE, FAKE, 0, NULL) == 2     # N % 128
+    assert q(FAKE, 128, 130, FAKE, FAKE, FAKE, FAKE, 0, NULL) == 2     # K % 128
+    assert q(FAKE, 128, 128, FAKE, FAKE, FAKE, FAKE, 2, NULL) == 1     # unknown mode
+    assert q(FAKE, 128, 128, FAKE, FAKE, NULL, FAKE, 0, NULL) == 1     # null transposed codes
+    assert q(FAKE, 128, 128, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1     # null transposed scales
+    assert q(FAKE, 128, 128, FAKE, FAKE, MISAL, FAKE, 0, NULL) == 1    # misaligned transposed codes
+    assert q(FAKE, 128, 128, NULL, FAKE, FAKE, FAKE, 0, NULL) == 1     # null codes
+    assert q(NULL, 0, 128, NULL, NULL, NULL, NULL, 1, NULL) == 0       # N == 0: no-op
+    b = L.quant_w_128x128_dual_batched
+    assert b(-1, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 1
+    assert b(0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 0
+    arr = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    Ns = (ctypes.c_int64 * 2)(128, 128)
+    Ks = (ctypes.c_int64 * 2)(128, 128)
+    assert b(2, arr, Ns, Ks, arr, arr, NULL, arr, 0, NULL) == 1        # null transposed-codes array
+    bad = (ctypes.c_void_p * 2)(0x10000, 0x20008)
+    assert b(2, arr, Ns, Ks, arr, arr, bad, arr, 0, NULL) == 1         # second tensor misaligned
+
+
 def test_gemm_validation(fp8bs):
     L = fp8bs.lib()
     g = L.fp8_block_gemm

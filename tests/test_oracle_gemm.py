@@ -50,6 +50,24 @@ def test_gemm_equals_matmul_of_dequantized(orc, shape, mode):
         assert np.max(np.abs(y - ref.T)) > 1e-3 * rms
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_data_gradient_from_transposed_weight_blocks(orc, mode):
+    """dX = dY W: the oracle's GEMM of quant_act(dY) with the quantization of
+    W^T equals the fp64 product dequant(dY) @ dequant(W) -- W's own blocks,
+    untransposed -- since a 128x128 block and its transpose share amax and scale."""
+    M, N, K = 130, 384, 256
+    dy = synth.activations(M, N, seed=7, sub=synth.SUB_DY)
+    w = synth.weights(N, K, seed=7, sub=synth.SUB_W)
+    dyq, dys = orc.quant_act_1x128(dy, mode)
+    wqt, wst = orc.quant_w_128x128(np.ascontiguousarray(w.T), mode)
+    dx = orc.gemm(dyq, dys, wqt, wst)
+    wq, ws = orc.quant_w_128x128(w, mode)
+    ref = _dequant_rows(orc, dyq, dys) @ _dequant_tiles(orc, wq, ws)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert dx.shape == (M, K) and rms > 0
+    assert np.max(np.abs(dx - ref)) <= 1e-12 * rms * np.sqrt(N)
+
+
 def test_gemm_integer_special_case(orc):
     """All scales 1 and codes of small integers: Y is an exact integer matmul."""
     g = np.random.default_rng(5)
