@@ -14,8 +14,9 @@ Workloads (--workload):
          64 rows, i.e. gate+up); the separate quantizer and GEMM calls are
          timed after the step for comparison.
   train  training backward of the dense layer: W and W^T codes from one
-         batched recalibration launch, quantization of the four output
-         gradients dY, and the four data-gradient GEMMs dX = dY W.
+         batched recalibration launch; per layer the quantization of dY, the
+         data-gradient GEMM dX = dY W, the quantization of dY^T and X^T along
+         the tokens and the weight-gradient GEMM dW = dY^T X.
   moe    MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens
          routed top-8: expert-weight recalibration, quantization of the
          gate+up and down inputs, the two grouped GEMMs.
@@ -201,11 +202,19 @@ def train_workload(fp8bs, dev, mode):
                 torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
                 torch.empty((K, N), dtype=torch.uint8, device=dev),
                 torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev))
+        x = bf16_dev(synth.activations(M, K, sub=synth.SUB_X + 10 * i), dev)
         dyq = torch.empty((M, N), dtype=torch.uint8, device=dev)
         dys = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        # the GEMM runs with the forward (N, K) swapped: output width K, reduction over N
-        bufs.append(dict(name=name, M=M, N=K, K=N, dy=dy, w=w, outs=outs, dyq=dyq, dys=dys, dx=dx))
+        # weight gradient: dY^T and X^T quantized along the tokens, dW [N, K]
+        dyt = (torch.empty((N, M), dtype=torch.uint8, device=dev),
+               torch.empty((N, M // 128), dtype=torch.float32, device=dev))
+        xt = (torch.empty((K, M), dtype=torch.uint8, device=dev),
+              torch.empty((K, M // 128), dtype=torch.float32, device=dev))
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        # the data-gradient GEMM runs with the forward (N, K) swapped: output width K, reduction over N
+        bufs.append(dict(name=name, M=M, N=K, K=N, dy=dy, w=w, x=x, outs=outs, dyq=dyq, dys=dys, dx=dx,
+                         dyt=dyt, xt=xt, dw=dw))
 
     w_all = [b["w"] for b in bufs]
     out_all = [b["outs"] for b in bufs]
@@ -218,9 +227,42 @@ def train_workload(fp8bs, dev, mode):
                   lambda: fp8bs.quant_act_1x128(b["dy"], mode, out=(b["dyq"], b["dys"])))
             maybe(timer, "gemm_" + b["name"],
                   lambda: gemm(b["dyq"], b["dys"], b["outs"][2], b["outs"][3], out=b["dx"]))
+            maybe(timer, "quant_act_t_dy_" + b["name"], lambda: fp8bs.quant_act_1x128_t(b["dy"], mode, out=b["dyt"]))
+            maybe(timer, "quant_act_t_x_" + b["name"], lambda: fp8bs.quant_act_1x128_t(b["x"], mode, out=b["xt"]))
+            maybe(timer, "wgrad_" + b["name"],
+                  lambda: fp8bs.fp8_block_gemm_1x128(b["dyt"][0], b["dyt"][1], b["xt"][0], b["xt"][1], out=b["dw"]))
 
-    flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
+    # data and weight gradients: twice the forward FLOPs
+    flops = sum(4.0 * b["M"] * b["N"] * b["K"] for b in bufs)
     return step, bufs, flops
+
+
+def summarize_train(bufs, timer):
+    """The data-gradient half as summarize_dense, plus the weight-gradient GEMMs and
+    the transposing quantizers; the roofline object covers whichever GEMM kernel
+    takes more of the step."""
+    kernels, roof = summarize_dense(bufs, timer, dual=True)
+    w_ms, w_flops = [], []
+    for b in bufs:
+        M, N, K = b["M"], b["N"], b["K"]   # (tokens, forward K, forward N)
+        t = timer.avg_ms("wgrad_" + b["name"])
+        kernels["wgrad_" + b["name"]] = mfma_entry(t, 2.0 * M * N * K)
+        w_ms.append(t)
+        w_flops.append(2.0 * M * N * K)
+        for what, width in (("dy", K), ("x", N)):
+            kernels["quant_act_t_%s_%s" % (what, b["name"])] = hbm_entry(
+                timer.avg_ms("quant_act_t_%s_%s" % (what, b["name"])), M * width * 3 + (M * width // 128) * 4)
+    d_ms = roof["avg_launch_ms"] * len(bufs)
+    if sum(w_ms) > d_ms:
+        mean_ms, mean_flops = sum(w_ms) / len(w_ms), sum(w_flops) / len(w_flops)
+        ach = mean_flops / (mean_ms * 1e-3) / 1e12
+        roof = {"kernel": "fp8bs::gemm_kernel<128, 128, 2, 2, false, false, true> (weight gradients of QKV, "
+                          "gate+up, down, o_proj over 8192 tokens)", "bound": "mfma",
+                "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "algorithmic_flop_per_launch": mean_flops, "avg_launch_ms": round(mean_ms, 4),
+                "traffic_source": None}
+    return kernels, roof
 
 
 def summarize_dense(bufs, timer, dual=False):
@@ -523,12 +565,13 @@ def main():
     elif args.workload == "train":
         step, bufs, flops = train_workload(fp8bs, dev, args.mode)
         ms = timed_loop(step, args.steps, args.warmup, timer)
-        kernels, roof = summarize_dense(bufs, timer, dual=True)
+        kernels, roof = summarize_train(bufs, timer)
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "training backward of the 8B-shaped dense layer at M=8192 tokens: "
-                                      "recalibrate 4 weights to W and W^T codes (one batched launch), quantize "
-                                      "4 output gradients dY (1x128 along N), data-gradient GEMMs dX = dY W for "
+                                      "recalibrate 4 weights to W and W^T codes (one batched launch); per layer "
+                                      "quantize dY (1x128 along N), data-gradient GEMM dX = dY W, quantize dY^T "
+                                      "and X^T (1x128 along the tokens), weight-gradient GEMM dW = dY^T X; "
                                       "QKV, gate+up, down, o_proj",
                           "scale_mode": "pow2" if args.mode else "exact", "out_dtype": "bf16",
                           "gemm_flops_per_step": flops},

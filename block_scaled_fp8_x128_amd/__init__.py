@@ -33,11 +33,13 @@ OUT_FP32 = 1
 # The functions declared in include/fp8bs.h, in declaration order.
 EXPORTS = (
     "quant_act_1x128",
+    "quant_act_1x128_t",
     "quant_w_128x128",
     "quant_w_128x128_batched",
     "quant_w_128x128_dual",
     "quant_w_128x128_dual_batched",
     "fp8_block_gemm",
+    "fp8_block_gemm_1x128",
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_pow2",
     "fp8_block_grouped_gemm_pow2",
@@ -68,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         L.quant_act_1x128.argtypes = [P, I64, I64, P, P, I32, P]
+        L.quant_act_1x128_t.argtypes = [P, I64, I64, P, P, I32, P]
+        L.fp8_block_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
         L.quant_w_128x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
@@ -87,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.argtypes = [I32]
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
-        for fn in ("quant_act_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
+        for fn in ("quant_act_1x128", "quant_act_1x128_t", "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
@@ -156,6 +160,21 @@ def quant_act_1x128(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
         xq, xs = out
     _check("quant_act_1x128", lib().quant_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(xs), int(mode), _stream(x)))
     return xq, xs
+
+
+def quant_act_1x128_t(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 [M, K] -> quant_act_1x128 of X^T: (codes uint8 [K, M], scales fp32 [K, M/128])."""
+    x = _bf16_payload(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    if out is None:
+        xqt = torch.empty((K, M), dtype=torch.uint8, device=x.device)
+        xst = torch.empty((K, M // 128), dtype=torch.float32, device=x.device)
+    else:
+        xqt, xst = out
+    _check("quant_act_1x128_t", lib().quant_act_1x128_t(_ptr(x), M, K, _ptr(xqt), _ptr(xst), int(mode), _stream(x)))
+    return xqt, xst
 
 
 def quant_w_128x128(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):
@@ -265,6 +284,23 @@ def fp8_block_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, workspace
 def fp8_block_gemm_pow2(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, workspace=None):
     """fp8_block_gemm for power-of-2 scales (POW2-quantized operands): the scales go to the matrix cores."""
     return _gemm("fp8_block_gemm_pow2", xq, xs, wq, ws, out_dtype, out, workspace)
+
+
+def fp8_block_gemm_1x128(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None):
+    """Y [M, N] with 1x128 scales on both operands (ws [N, K/128]): the weight gradient
+    dW = dY^T X from quant_act_1x128_t(dY) and quant_act_1x128_t(X)."""
+    xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
+    xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or xs.shape != (M, K // 128) or ws.shape != (N, K // 128):
+        raise ValueError("operand shapes do not match")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=xq.device)
+    _check("fp8_block_gemm_1x128", lib().fp8_block_gemm_1x128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
+                                                              _ptr(out), code, _stream(xq)))
+    return out
 
 
 def _gemm(fn, xq, xs, wq, ws, out_dtype, out, workspace):

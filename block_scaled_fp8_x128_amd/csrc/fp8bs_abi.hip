@@ -126,6 +126,23 @@ int quant_act_1x128(const void *x_bf16, int64_t M, int64_t K, void *xq, float *x
     return status_of(fp8bs::launch_quant_act(x_bf16, M, K, xq, xs, scale_mode, (hipStream_t)stream));
 }
 
+int quant_act_1x128_t(const void *x_bf16, int64_t M, int64_t K, void *xqt, float *xst, int scale_mode, void *stream)
+{
+    // X^T [K, M] in 1x128 blocks along M: M must be a multiple of 128 as well
+    if (M < 0 || K <= 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))
+        return FP8BS_INVALID_ARG;
+    if (M % 128 != 0 || K % 128 != 0 || (M / 128) * (K / 128) >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (M == 0)
+        return FP8BS_OK;
+    int st = check_quant(x_bf16, K, M, xqt, xst, scale_mode, false);
+    if (st != FP8BS_OK)
+        return st;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_quant_act_t(x_bf16, M, K, xqt, xst, scale_mode, (hipStream_t)stream));
+}
+
 int quant_w_128x128(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, int scale_mode, void *stream)
 {
     int st = check_quant(w_bf16, N, K, wq, ws, scale_mode, true);
@@ -231,6 +248,23 @@ int quant_w_128x128_dual_batched(int64_t count, const void *const *w_bf16, const
                                  int scale_mode, void *stream)
 {
     return quant_w_dual_impl(count, w_bf16, N, K, wq, ws, wqt, wst, scale_mode, stream);
+}
+
+int fp8_block_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                         int64_t K, void *y, int out_dtype, void *stream)
+{
+    int st = check_gemm_common(xq, xs, y, M, N, K, out_dtype);
+    if (st != FP8BS_OK)
+        return st;
+    // per-row weight scales: [N, K/128]
+    if (!tensor_ok(wq, N * K, 16) || !tensor_ok(ws, N * K, 4))
+        return FP8BS_INVALID_ARG;
+    if (M == 0)
+        return FP8BS_OK;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_gemm_1x128(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32,
+                                              (hipStream_t)stream));
 }
 
 size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K)

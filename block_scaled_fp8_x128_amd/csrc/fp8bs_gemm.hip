@@ -236,7 +236,11 @@ __global__ __launch_bounds__(64) void grouped_tile_table_kernel(const int32_t *o
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED>
+// WROW: the weight operand carries one scale per row and K block (ws [N, K/128],
+// the 1x128 blocks of an activation-like operand: the weight gradient, whose
+// both operands are quantized along the tokens), so the scale product differs
+// per output column; each lane forms xs * ws for its 4 columns of a tile.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool WROW = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
 {
     using C = GemmCfg<BM, BN, WAVES_M, WAVES_N>;
@@ -308,6 +312,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
         xs_row[i] = a.xs + gr * KB;
     }
     const float *ws_row = ws + ((n0 + wn * C::WN) / 128) * KB;
+    // WROW: the scales of this lane's 4 columns (rows of W) of each n-tile
+    const float *ws_col[WROW ? C::TN : 1];
+    if constexpr (WROW) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            ws_col[j] = ws + (n0 + wn * C::WN + j * 16 + fg * 4) * KB;
+    }
 
     v4f acc[C::TM][C::TN];
 #pragma unroll
@@ -333,11 +344,17 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
             for (int j = 0; j < C::LOADS; ++j)
                 stage[j] = *(const u32x4 *)(src[j] + (kb + 1) * BK);
         }
-        const float sw = ws_row[kb];
+        const float sw = WROW ? 1.0f : ws_row[kb];
         float sc[C::TM];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
             sc[i] = xs_row[i][kb] * sw;
+        v4f swv[WROW ? C::TN : 1];
+        if constexpr (WROW) {
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                swv[j] = v4f{ws_col[j][kb], ws_col[j][KB + kb], ws_col[j][2 * KB + kb], ws_col[j][3 * KB + kb]};
+        }
 
         const uint8_t *L = lds + cur * C::STAGE_BYTES;
         v8i bx[C::TM], aw[C::TN];
@@ -360,7 +377,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
                 // format 0 = FP8 E4M3 for both operands; scale operands 0: the plain (unscaled) MFMA
                 const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[j], bx[i], v4f{0.f, 0.f, 0.f, 0.f},
                                                                                0, 0, 0, 0, 0, 0);
-                acc[i][j] = __builtin_elementwise_fma(v4f{sc[i], sc[i], sc[i], sc[i]}, p, acc[i][j]);
+                const v4f scv = v4f{sc[i], sc[i], sc[i], sc[i]};
+                if constexpr (WROW)
+                    acc[i][j] = __builtin_elementwise_fma(scv * swv[j], p, acc[i][j]);
+                else
+                    acc[i][j] = __builtin_elementwise_fma(scv, p, acc[i][j]);
             }
         }
         if (more) {
@@ -1485,6 +1506,30 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
     default:
         return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
     }
+}
+
+hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                             int64_t K, void *y, int out_fp32, hipStream_t stream)
+{
+    if (M == 0)
+        return hipSuccess;
+    GemmArgs a = {};
+    a.xq = (const uint8_t *)xq;
+    a.xs = xs;
+    a.wq = (const uint8_t *)wq;
+    a.ws = ws;
+    a.y = y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.tiles_m = (int)((M + 127) / 128);
+    a.tiles_n = (int)(N / 128);
+    a.ksplit = 1;
+    const int grid = a.tiles_m * a.tiles_n;
+    const dim3 block(2 * 2 * 64);
+    if (out_fp32)
+        return launch(gemm_kernel<128, 128, 2, 2, true, false, true>, dim3(grid), block, 0, stream, a);
+    return launch(gemm_kernel<128, 128, 2, 2, false, false, true>, dim3(grid), block, 0, stream, a);
 }
 
 // ---- the whole linear layer: bf16 activations in ---------------------------------

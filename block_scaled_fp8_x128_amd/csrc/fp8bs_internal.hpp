@@ -30,6 +30,9 @@ static inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, s
 // ---- quantizers (fp8bs_quant.hip) ------------------------------------------
 
 hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float *xs, int mode, hipStream_t stream);
+// quant_act_1x128 of X^T: codes [K, M], scales [K, M/128] (M, K multiples of 128).
+hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, float *xst, int mode,
+                              hipStream_t stream);
 
 // One weight tensor of a batched weight quantization (qt, st: the transposed
 // codes [K, N] and scales [K/128, N/128], written by the dual launcher only).
@@ -54,6 +57,10 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 // through the matrix cores' E8M0 operands where they can)
 hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
                        int64_t K, void *y, int out_fp32, int pow2, void *workspace, hipStream_t stream);
+// The product with per-row weight scales ws [N, K/128] (both operands in
+// 1x128 blocks along K): the weight gradient.
+hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                             int64_t K, void *y, int out_fp32, hipStream_t stream);
 // Y = fp8_block_gemm(quant_act_1x128(x), Wq, Ws) from bf16 x; the workspace
 // holds the quantized x (unless the shape runs fused) and the GEMM's own.
 size_t linear_workspace_size(int64_t M, int64_t N, int64_t K);

@@ -361,4 +361,77 @@ hipError_t launch_quant_w_dual(const WTensor *t, int64_t count, int mode, hipStr
     return hipSuccess;
 }
 
+// ---- activations for the weight gradient: 1x128 blocks along the rows ---------
+//
+// The weight gradient dW = dY^T X contracts over the tokens (the rows of X
+// and of dY), so both operands are quantized in 1x128 blocks that run down a
+// column: the quantization of X^T by quant_act_1x128's rule, written as X^T
+// [K, M] with the tokens contiguous.  A workgroup takes a 128 x 128 tile of X
+// (rows mb, columns kb): thread t loads chunk (t % 16) of rows
+// 8 (t / 16) .. + 7, transposes that 8x8 square of bf16 values in registers
+// and writes its 8 transposed row pieces into an LDS tile (piece g of row p
+// at slot g ^ (p / 8), so the 16 lanes of a write and of a read that share a
+// row or a piece index hit different banks).  The tile's 128 rows of X^T are
+// then 1x128 blocks, quantized exactly as quant_act_kernel does: a 16-lane
+// DPP row per block, one 16-byte chunk per lane.
+template <int MODE>
+__global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
+                                                                 float *__restrict__ s, int64_t M, int64_t K)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tl[128 * 256]; // the transposed bf16 tile
+    const int64_t KB = K / 128, MB = M / 128;
+    const int64_t mb = blockIdx.x / KB, kb = blockIdx.x % KB;
+    const int t = threadIdx.x;
+    const int rg = t >> 4, c = t & 15;
+    const int64_t base = (mb * 128 + 8 * rg) * K + kb * 128 + c * 8;
+
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = __builtin_nontemporal_load((const u32x4 *)(x + base + j * K));
+    // transposed row i (column 8 c + i of the tile) holds element i of rows
+    // 8 rg .. 8 rg + 7; its dword p pairs rows 2p (low half) and 2p + 1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 o;
+        o.x = __builtin_amdgcn_perm(v[1][i >> 1], v[0][i >> 1], sel);
+        o.y = __builtin_amdgcn_perm(v[3][i >> 1], v[2][i >> 1], sel);
+        o.z = __builtin_amdgcn_perm(v[5][i >> 1], v[4][i >> 1], sel);
+        o.w = __builtin_amdgcn_perm(v[7][i >> 1], v[6][i >> 1], sel);
+        const int p = 8 * c + i;
+        *(u32x4 *)(tl + p * 256 + ((rg ^ c) << 4)) = o;
+    }
+    __syncthreads();
+
+    const int lane = t & 63, wave = t >> 6;
+    const int g = lane & 15; // 16-byte chunk (8 tokens) of the block
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+        const int p = pass * 16 + wave * 4 + (lane >> 4); // row of X^T within the tile
+        const u32x4 val = *(const u32x4 *)(tl + p * 256 + ((g ^ (p >> 3)) << 4));
+        const float amax = amax_value(row16_max(chunk_max_mag(val)));
+        BlockQuant<MODE> bq;
+        bq.init(amax);
+        const u32x2 codes = quant_chunk<MODE>(val, bq);
+        const int64_t row = kb * 128 + p;
+        __builtin_nontemporal_store(codes, (u32x2 *)(q + row * M + mb * 128 + 8 * g));
+        if (g == 0)
+            s[row * MB + mb] = bq.s;
+    }
+}
+
+hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, float *xst, int mode,
+                              hipStream_t stream)
+{
+    const int64_t tiles = (M / 128) * (K / 128);
+    if (tiles == 0)
+        return hipSuccess;
+    if (mode == SCALE_POW2)
+        return launch(quant_act_t_kernel<SCALE_POW2>, dim3((unsigned)tiles), dim3(QW_THREADS), 0, stream,
+                      (const uint16_t *)x, (uint8_t *)xqt, xst, M, K);
+    return launch(quant_act_t_kernel<SCALE_EXACT>, dim3((unsigned)tiles), dim3(QW_THREADS), 0, stream,
+                  (const uint16_t *)x, (uint8_t *)xqt, xst, M, K);
+}
+
 } // namespace fp8bs

@@ -96,6 +96,25 @@ FP8BS_API int quant_act_1x128(const void *x_bf16, int64_t M, int64_t K, void *xq
                     void *stream);
 
 /*
+ * quant_act_1x128_t -- quant_act_1x128 of the transpose: X [M, K] quantized
+ * in 1x128 blocks that run down its columns (128 consecutive rows of one
+ * column), written transposed.  The weight gradient dW = dY^T X of a
+ * training step contracts over the tokens, so both of its operands are
+ * quantized along them (the article's recipe runs FP8 in training as well,
+ * section "Technical breakthrough"; the block runs along the reduction
+ * dimension, as the 1x128 activation block does in the forward product).
+ *
+ *   x_bf16 : [M, K] bf16 payloads (input), M and K multiples of 128
+ *   xqt    : [K, M] E4M3 codes, row k = the codes of column k of X
+ *   xst    : [K, M/128] fp32 scales; xst[k, mb] covers X[128 mb .. 128 mb + 127, k]
+ * Bit for bit quant_act_1x128 of the transposed matrix (the same element
+ * rule, amax over a block's 128 values).  Errors: as quant_act_1x128, and
+ * UNSUPPORTED_SHAPE if M % 128 != 0.  M == 0 is a no-op.
+ */
+FP8BS_API int quant_act_1x128_t(const void *x_bf16, int64_t M, int64_t K, void *xqt, float *xst, int scale_mode,
+                                void *stream);
+
+/*
  * quant_w_128x128 -- weight quantizer, one scale per 128x128 block (article
  * section "Technical breakthrough": 128x128 granularity for weights).  Called
  * on every weight after each optimizer step, it is the per-step scale
@@ -189,6 +208,23 @@ FP8BS_API int quant_w_128x128_dual_batched(int64_t count, const void *const *w_b
 FP8BS_API int fp8_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
                    int64_t K, void *y, int out_dtype, void *workspace, size_t workspace_bytes,
                    void *stream);
+
+/*
+ * fp8_block_gemm_1x128 -- fp8_block_gemm with 1x128 scales on both operands:
+ *   Y[m, n] = sum_kb (xs[m, kb] * ws[n, kb]) * P[m, n, kb],
+ * ws [N, K/128] holding one scale per row of wq and K block.  This is the
+ * weight gradient of a training step, dW = dY^T X, with
+ *   xq, xs = quant_act_1x128_t(dY)  ([N_out, M_tok], rows of dY^T),
+ *   wq, ws = quant_act_1x128_t(X)   ([K_in, M_tok], rows of X^T),
+ * so M = N_out, N = K_in, K = M_tok and Y [N_out, K_in] is dW.  The scale
+ * product is formed in fp32 per output element and K block, then applied by
+ * one fp32 FMA into the accumulator.  The bf16 output is the round to
+ * nearest even of the fp32 output.  Errors: INVALID_ARG, UNSUPPORTED_SHAPE
+ * (N or K not a multiple of 128), UNSUPPORTED_DEVICE, HIP_ERROR.  No
+ * workspace.  M == 0 is a no-op.
+ */
+FP8BS_API int fp8_block_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M,
+                                   int64_t N, int64_t K, void *y, int out_dtype, void *stream);
 
 /*
  * fp8_block_grouped_gemm -- the MoE (mixture-of-experts) form of

@@ -59,6 +59,8 @@ def lib():
         L.oracle_quant_w_128x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
         L.oracle_gemm.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.oracle_gemm_sampled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
+        L.oracle_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_gemm_1x128_sampled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.oracle_grouped_gemm_sampled.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P, I64, P]
         L.oracle_max_threads.restype = ctypes.c_int
@@ -141,6 +143,12 @@ def quant_w_128x128(w_bf16, mode: int = SCALE_EXACT):
     return q, s
 
 
+def quant_act_1x128_t(x_bf16, mode: int = SCALE_EXACT):
+    """quant_act_1x128 of X^T: 1x128 blocks down the columns of X [M, K], written as
+    codes [K, M] and scales [K, M/128] (the weight gradient's operands)."""
+    return quant_act_1x128(np.ascontiguousarray(np.asarray(x_bf16).T), mode)
+
+
 # ---- GEMMs ---------------------------------------------------------------------
 
 def gemm(xq, xs, wq, ws) -> np.ndarray:
@@ -168,6 +176,30 @@ def gemm_sampled(xq, xs, wq, ws, rows, cols) -> np.ndarray:
     y = np.empty(rows.shape, dtype=np.float64)
     lib().oracle_gemm_sampled(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
                               _ptr(rows), _ptr(cols), rows.size, _ptr(y))
+    return y
+
+
+def gemm_1x128(xq, xs, wq, ws) -> np.ndarray:
+    """fp64 Y [M, N] with 1x128 scales on both operands: ws [N, K/128]."""
+    xq, wq = _c(xq, np.uint8), _c(wq, np.uint8)
+    xs, ws = _c(xs, np.float32), _c(ws, np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_gemm_1x128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y))
+    return y
+
+
+def gemm_1x128_sampled(xq, xs, wq, ws, rows, cols) -> np.ndarray:
+    xq, wq = _c(xq, np.uint8), _c(wq, np.uint8)
+    xs, ws = _c(xs, np.float32), _c(ws, np.float32)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty(rows.shape, dtype=np.float64)
+    lib().oracle_gemm_1x128_sampled(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
+                                    _ptr(rows), _ptr(cols), rows.size, _ptr(y))
     return y
 
 

@@ -38,7 +38,10 @@
  *                        invariants, error bound, brute force on tiny shapes,
  *                        torch's fp32 division + fp8 cast;
  *   gemm, grouped_gemm : numpy fp64 matmul of the dequantized operands,
- *                        integer special cases, per-expert decomposition.
+ *                        integer special cases, per-expert decomposition;
+ *   gemm_1x128         : numpy fp64 matmul of the dequantized operands (row
+ *                        scales on both), the block-scaled gemm where the row
+ *                        scales are constant over 128 rows, integer case.
  */
 #include <math.h>
 #include <stdint.h>
@@ -237,8 +240,8 @@ static int e4m3_times_512(uint32_t c, int *is_nan)
  * blocks taken in ascending kb.  READING: the article says only that linear
  * layers run FP8 math; the per-128-K application of the product of the two
  * fp32 scales is the project's statement of the GEMM. */
-static double gemm_element(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
-                           int64_t K, int64_t m, int64_t n)
+static double gemm_element_g(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                             int64_t K, int64_t m, int64_t n, int64_t ws_row)
 {
     int64_t KB = K / 128, kb, k;
     double y = 0.0;
@@ -247,9 +250,16 @@ static double gemm_element(const uint8_t *xq, const float *xs, const uint8_t *wq
         int64_t p = 0;
         for (k = kb * 128; k < kb * 128 + 128; ++k)
             p += (int64_t)e4m3_times_512(xq[m * K + k], &nan) * (int64_t)e4m3_times_512(wq[n * K + k], &nan);
-        y += ((double)xs[m * KB + kb] * (double)ws[(n / 128) * KB + kb]) * ldexp((double)p, -18);
+        y += ((double)xs[m * KB + kb] * (double)ws[ws_row * KB + kb]) * ldexp((double)p, -18);
     }
     return nan ? NAN : y;
+}
+
+/* Weight scales per 128x128 block: row n of wq takes the scales of block row n/128. */
+static double gemm_element(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                           int64_t K, int64_t m, int64_t n)
+{
+    return gemm_element_g(xq, xs, wq, ws, K, m, n, n / 128);
 }
 
 /* Y = Xq Wq^T with block scales.  xq [M, K], xs [M, K/128], wq [N, K],
@@ -274,6 +284,33 @@ void oracle_gemm_sampled(const uint8_t *xq, const float *xs, const uint8_t *wq, 
 #pragma omp parallel for schedule(dynamic, 16)
     for (i = 0; i < count; ++i)
         y[i] = gemm_element(xq, xs, wq, ws, K, rows[i], cols[i]);
+}
+
+/* The same product with 1x128 scales on both operands: ws [N, K/128] holds one
+ * scale per row of wq and K block (the weight gradient dW = dY^T X, both of
+ * whose operands are activation-like and quantized along the tokens).
+ * READING: the article says its recipe also runs in training but not how the
+ * backward products are blocked; the 1x128 block along the reduction
+ * dimension, as for the forward activations, is the project's reading. */
+void oracle_gemm_1x128(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                       int64_t M, int64_t N, int64_t K, double *y)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M * N; ++i)
+        y[i] = gemm_element_g(xq, xs, wq, ws, K, i / N, i % N, i % N);
+}
+
+void oracle_gemm_1x128_sampled(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                               int64_t M, int64_t N, int64_t K, const int64_t *rows, const int64_t *cols,
+                               int64_t count, double *y)
+{
+    int64_t i;
+    (void)M;
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i)
+        y[i] = gemm_element_g(xq, xs, wq, ws, K, rows[i], cols[i], cols[i]);
 }
 
 /* Grouped (MoE) GEMM: rows offs[e] .. offs[e+1]-1 of (xq, xs) use expert e's

@@ -11,6 +11,11 @@ import numpy as np
 import torch
 
 GEMM_TOL = 1e-2
+# Internal precision of the FP8 matrix-core dot product: the 128 products of
+# a K block are not summed exactly; measured deviations stay below 2^-12 of
+# the block's sum of |products| (a pin in test_gpu_train checks 2^-11 on
+# crafted worst cases).  Used where both operands carry outliers.
+MFMA_DOT_TAU = 2.0 ** -11
 
 
 def dev():
@@ -66,3 +71,17 @@ def sample_positions(M, N, count, seed=0, block=128):
     rows = [rr.reshape(-1), g.integers(0, M, count)]
     cols = [cc.reshape(-1), g.integers(0, N, count)]
     return np.concatenate(rows), np.concatenate(cols)
+
+
+def gemm_gate_abs(name, y_gpu: np.ndarray, y_ref: np.ndarray, abs_sum: np.ndarray, tol: float = GEMM_TOL,
+                  tau: float = MFMA_DOT_TAU):
+    """Per element |err| <= tol * rms(oracle) + tau * abs_sum, abs_sum being the
+    oracle's sum over K blocks of |scale product| * sum |decoded products| (the
+    standard dot-product error bound, with the matrix core's internal
+    precision as the relative factor).  Reports the plain max|err|/rms too."""
+    rms = float(np.sqrt(np.mean(np.square(y_ref))))
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bound = tol * rms + tau * abs_sum
+    say("%s: max|err|/rms = %.3e, max err/bound = %.3f" % (name, float(err.max()) / rms, float((err / bound).max())))
+    assert np.isfinite(y_gpu).all()
+    assert (err <= bound).all(), (name, int((err > bound).sum()))

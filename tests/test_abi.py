@@ -131,6 +131,24 @@ def test_quant_w_dual_validation(fp8bs):
     assert b(2, arr, Ns, Ks, arr, arr, bad, arr, 0, NULL) == 1         # second tensor misaligned
 
 
+def test_weight_gradient_entry_validation(fp8bs):
+    L = fp8bs.lib()
+    q = L.quant_act_1x128_t
+    assert q(FAKE, 100, 128, FAKE, FAKE, 0, NULL) == 2     # M % 128 (blocks run down the columns)
+    assert q(FAKE, 128, 100, FAKE, FAKE, 0, NULL) == 2     # K % 128
+    assert q(FAKE, 128, 128, FAKE, FAKE, 3, NULL) == 1     # unknown mode
+    assert q(FAKE, 128, 128, NULL, FAKE, 0, NULL) == 1     # null codes
+    assert q(MISAL, 128, 128, FAKE, FAKE, 0, NULL) == 1    # misaligned input
+    assert q(NULL, 0, 128, NULL, NULL, 0, NULL) == 0       # M == 0: no-op
+    g = L.fp8_block_gemm_1x128
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 100, 128, FAKE, 0, NULL) == 2   # N % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 100, FAKE, 0, NULL) == 2   # K % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 128, 128, FAKE, 0, NULL) == 1  # M < 0
+    assert g(FAKE, FAKE, FAKE, NULL, 8, 128, 128, FAKE, 0, NULL) == 1   # null weight scales
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 128, MISAL, 0, NULL) == 1  # misaligned output
+    assert g(NULL, NULL, FAKE, FAKE, 0, 128, 128, NULL, 0, NULL) == 0   # M == 0: no-op
+
+
 def test_gemm_validation(fp8bs):
     L = fp8bs.lib()
     g = L.fp8_block_gemm

@@ -1,4 +1,4 @@
-"""GPU parity of the training path's weight quantizer and data-gradient product.
+"""GPU parity of the training path: the data and weight gradients' quantizers and products.
 
 quant_w_128x128_dual writes the codes and scales of W and of W^T from one read
 of W.  Bar: bit-exact against the oracle -- (wq, ws) against its quantization
@@ -7,7 +7,14 @@ shapes) or, at full size, against the transpose of its quantization of W
 (the oracle's transpose symmetry is pinned on the CPU).  The data gradient
 dX = dY W runs fp8_block_gemm on quant_act_1x128(dY) and (wqt, wst); its gate
 is the GEMM gate against the oracle's fp64 product of the same quantized
-operands.
+operands.  The weight gradient dW = dY^T X quantizes both operands with
+quant_act_1x128_t (bit-exact against the oracle's quant_act_1x128 of the
+transposed matrix) and multiplies them with fp8_block_gemm_1x128.  Both of
+its operands carry the x50 outliers, whose coinciding products make some
+outputs ~100x the rms; there the matrix core's own dot-product precision
+(below 2^-12 of a block's sum of |products|, pinned here) exceeds 1e-2 * rms,
+so its gate adds the standard dot-product term tau * sum |products|
+(tau = 2^-11) to the 1e-2 * rms of the forward GEMM gate.
 """
 
 import numpy as np
@@ -15,7 +22,8 @@ import pytest
 import torch
 
 import synth
-from gpu_util import assert_bitexact, bf16_to_dev, gemm_gate, host, sample_positions, say
+from gpu_util import (MFMA_DOT_TAU, assert_bitexact, bf16_to_dev, gemm_gate, gemm_gate_abs, host, sample_positions,
+                      say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +127,97 @@ def test_dgrad_parity_full_size_sampled(fp8bs, orc, case):
     rows, cols = sample_positions(M, K, 3000, seed=M + N + K)
     ref = orc.gemm_sampled(dyq_r, dys_r, wqt_r, wst_r, rows, cols)
     gemm_gate("dX fp32 (sampled %d)" % rows.size, host(dx32)[rows, cols], ref)
+
+
+# ---- weight gradient: dW = dY^T X, both operands in 1x128 blocks along the tokens ----
+
+ACT_T_SHAPES = [(128, 128), (256, 512), (384, 1152), (1024, 768), (8192, 4096), (8192, 28672)]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", ACT_T_SHAPES, ids=lambda s: "%dx%d" % s)
+def test_quant_act_t_parity(fp8bs, orc, shape, mode):
+    M, K = shape
+    say("quant_act_1x128_t M=%d K=%d mode=%d" % (M, K, mode))
+    x = synth.activations(M, K, seed=synth.SEED, sub=synth.SUB_X)
+    q_ref, s_ref = orc.quant_act_1x128_t(x, mode)
+    q, s = fp8bs.quant_act_1x128_t(bf16_to_dev(x), mode)
+    assert_bitexact("codes", host(q), q_ref)
+    assert_bitexact("scales", host(s), s_ref)
+
+
+def _wgrad(fp8bs, orc, M, N, K, mode):
+    """dW [N, K] = dY [M, N]^T X [M, K] over M tokens."""
+    dy = synth.activations(M, N, seed=synth.SEED, sub=synth.SUB_DY)
+    x = synth.activations(M, K, seed=synth.SEED, sub=synth.SUB_X)
+    dyq, dys = fp8bs.quant_act_1x128_t(bf16_to_dev(dy), mode)
+    xq, xs = fp8bs.quant_act_1x128_t(bf16_to_dev(x), mode)
+    dw32 = fp8bs.fp8_block_gemm_1x128(dyq, dys, xq, xs, out_dtype=torch.float32)
+    dw16 = fp8bs.fp8_block_gemm_1x128(dyq, dys, xq, xs, out_dtype=torch.bfloat16)
+    assert torch.equal(dw16.view(torch.int16), dw32.to(torch.bfloat16).view(torch.int16))
+    dw32b = fp8bs.fp8_block_gemm_1x128(dyq, dys, xq, xs, out_dtype=torch.float32)
+    assert torch.equal(dw32.view(torch.int32), dw32b.view(torch.int32))
+    dyq_r, dys_r = orc.quant_act_1x128_t(dy, mode)
+    xq_r, xs_r = orc.quant_act_1x128_t(x, mode)
+    assert_bitexact("dyq", host(dyq), dyq_r)
+    assert_bitexact("xq", host(xq), xq_r)
+    return dw32, dyq_r, dys_r, xq_r, xs_r
+
+
+def test_mfma_dot_product_precision(fp8bs, orc):
+    """Pins the relative factor of the weight-gradient gate: one dominant product
+    (448 x 448) beside 127 small ones, and one K block of the outlier data, each
+    within MFMA_DOT_TAU of their sum of |products| on the matrix cores."""
+    dec = orc.e4m3_decode_array
+    cases = []
+    for small in (0x38, 0x30, 0x28, 0x20, 0x10, 0x08, 0x01):
+        a = np.full(128, small, np.uint8)
+        b = np.full(128, 0x38, np.uint8)
+        a[0] = b[0] = 0x7E
+        cases.append((a, b))
+    g = np.random.default_rng(3)
+    for _ in range(8):        # random codes of both signs, one +-448 x +-448 product each
+        a = g.integers(0, 0x7E, 128).astype(np.uint8) | (g.integers(0, 2, 128) << 7).astype(np.uint8)
+        b = g.integers(0, 0x7E, 128).astype(np.uint8) | (g.integers(0, 2, 128) << 7).astype(np.uint8)
+        a[5], b[5] = 0x7E, 0xFE
+        cases.append((a, b))
+    worst = 0.0
+    for a, b in cases:
+        A = np.zeros((1, 128), np.uint8)
+        B = np.zeros((128, 128), np.uint8)
+        A[0], B[0] = a, b
+        y = host(fp8bs.fp8_block_gemm_1x128(to_dev(A), to_dev(np.ones((1, 1), np.float32)), to_dev(B),
+                                            to_dev(np.ones((128, 1), np.float32)), out_dtype=torch.float32))[0, 0]
+        prods = dec(a).astype(np.float64) * dec(b).astype(np.float64)
+        rel = abs(float(y) - prods.sum()) / np.abs(prods).sum()
+        worst = max(worst, rel)
+    say("FP8 MFMA dot product: worst |P_gpu - P| / sum|products| = %.3e (2^%.1f)" % (worst, np.log2(max(worst, 1e-30))))
+    assert worst <= MFMA_DOT_TAU
+
+
+def _abs_codes(q):
+    return q & np.uint8(0x7F)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", [(256, 256, 384), (384, 512, 128), (128, 128, 256), (640, 1152, 384)],
+                         ids=lambda s: "%dx%dx%d" % s)
+def test_wgrad_parity_full_output(fp8bs, orc, shape, mode):
+    M, N, K = shape
+    say("wgrad tokens=%d N=%d K=%d mode=%d" % (M, N, K, mode))
+    dw32, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, mode)
+    ref = orc.gemm_1x128(dyq_r, dys_r, xq_r, xs_r)
+    abs_sum = orc.gemm_1x128(_abs_codes(dyq_r), dys_r, _abs_codes(xq_r), xs_r)
+    gemm_gate_abs("dW fp32", host(dw32), ref, abs_sum)
+
+
+@pytest.mark.parametrize("case", DGRAD_LARGE, ids=lambda c: c[0])
+def test_wgrad_parity_full_size_sampled(fp8bs, orc, case):
+    name, N, K = case
+    M = 8192
+    say("wgrad %s tokens=%d N=%d K=%d" % (name, M, N, K))
+    dw32, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, 0)
+    rows, cols = sample_positions(N, K, 3000, seed=M + N + K)
+    ref = orc.gemm_1x128_sampled(dyq_r, dys_r, xq_r, xs_r, rows, cols)
+    abs_sum = orc.gemm_1x128_sampled(_abs_codes(dyq_r), dys_r, _abs_codes(xq_r), xs_r, rows, cols)
+    gemm_gate_abs("dW fp32 (sampled %d)" % rows.size, host(dw32)[rows, cols], ref, abs_sum)

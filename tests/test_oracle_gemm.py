@@ -68,6 +68,44 @@ def test_data_gradient_from_transposed_weight_blocks(orc, mode):
     assert np.max(np.abs(dx - ref)) <= 1e-12 * rms * np.sqrt(N)
 
 
+def _dequant_row_scaled(orc, q, s):
+    """decode(q) * s with s [R, K/128] broadcast over each row's 1x128 blocks."""
+    return orc.e4m3_decode_array(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_weight_gradient_closed_form(orc, mode):
+    """dW = dY^T X from quant_act_1x128_t of both: the oracle's 1x128 x 1x128 GEMM
+    equals the fp64 product of the dequantized operands, blocked down the tokens."""
+    M, N, K = 256, 384, 256          # tokens, output features, input features
+    dy = synth.activations(M, N, seed=11, sub=synth.SUB_DY)
+    x = synth.activations(M, K, seed=11, sub=synth.SUB_X)
+    dyq, dys = orc.quant_act_1x128_t(dy, mode)        # [N, M], [N, M/128]
+    xq, xs = orc.quant_act_1x128_t(x, mode)           # [K, M], [K, M/128]
+    assert dyq.shape == (N, M) and dys.shape == (N, M // 128) and xq.shape == (K, M)
+    dw = orc.gemm_1x128(dyq, dys, xq, xs)
+    ref = _dequant_row_scaled(orc, dyq, dys) @ _dequant_row_scaled(orc, xq, xs).T
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert dw.shape == (N, K) and rms > 0
+    assert np.max(np.abs(dw - ref)) <= 1e-12 * rms * np.sqrt(M)
+    # a block of the transposed quantization is a column block of X: its scale is the
+    # column's amax over 128 tokens
+    col = synth.bf16_bits_to_f32(x[:128, 5]).astype(np.float64)
+    assert xs[5, 0] == np.float32(orc.block_scale(float(np.max(np.abs(col))), mode))
+    # sampled positions agree with the full product
+    rows, cols = np.array([0, 17, 383, 200]), np.array([255, 0, 128, 77])
+    assert np.array_equal(orc.gemm_1x128_sampled(dyq, dys, xq, xs, rows, cols), dw[rows, cols])
+
+
+def test_gemm_1x128_reduces_to_block_scaled_gemm(orc):
+    """Row scales that are constant over each 128-row group are 128x128 block scales:
+    the two GEMMs then agree exactly."""
+    M, N, K = 130, 256, 384
+    xq, xs, wq, ws = _operands(orc, M, N, K, seed=3)
+    ws_rows = np.repeat(ws, 128, axis=0)               # [N, K/128]
+    assert np.array_equal(orc.gemm_1x128(xq, xs, wq, ws_rows), orc.gemm(xq, xs, wq, ws))
+
+
 def test_gemm_integer_special_case(orc):
     """All scales 1 and codes of small integers: Y is an exact integer matmul."""
     g = np.random.default_rng(5)
