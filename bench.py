@@ -60,7 +60,7 @@ COPY_BYTES = 1 << 30
 # Dominant kernel of each workload: (kernel-name prefix in a rocprofv3 trace,
 # source file, traffic record under profiles/).
 DOMINANT = {
-    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false>", GEMM_SRC,
+    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, false>", GEMM_SRC,
               "gemm_dma_256x256_dense_m8192_traffic.json"),
     "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
 }
@@ -256,8 +256,8 @@ def summarize_train(bufs, timer):
     if sum(w_ms) > d_ms:
         mean_ms, mean_flops = sum(w_ms) / len(w_ms), sum(w_flops) / len(w_flops)
         ach = mean_flops / (mean_ms * 1e-3) / 1e12
-        roof = {"kernel": "fp8bs::gemm_kernel<128, 128, 2, 2, false, false, true> (weight gradients of QKV, "
-                          "gate+up, down, o_proj over 8192 tokens)", "bound": "mfma",
+        roof = {"kernel": "fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, true> (weight "
+                          "gradients of QKV, gate+up, down, o_proj over 8192 tokens)", "bound": "mfma",
                 "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,
                 "algorithmic_flop_per_launch": mean_flops, "avg_launch_ms": round(mean_ms, 4),

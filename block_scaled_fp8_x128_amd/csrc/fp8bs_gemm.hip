@@ -453,7 +453,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_kernel(GemmArgs a)
 //     stages (16 rows x EPI_CW columns, rows padded by 16 bytes), so each
 //     store instruction writes whole 64- or 128-byte row segments instead of
 //     16 scattered 32-byte pieces.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES_>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES_, bool WROW_ = false>
 struct DmaCfg {
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = NW * 64;
@@ -466,7 +466,20 @@ struct DmaCfg {
     static constexpr int STAGE_BYTES = XS_OFF + NW * 256;    // 64 fp32 per wave
     static constexpr int XG = BM / 8 / NW; // 1 KiB row groups of X per wave per stage
     static constexpr int WG = BN / 8 / NW; // ... of W
-    static constexpr int DPW = XG + WG + 1; // LDS-DMA instructions per wave per stage (+1: scales)
+    // LDS-DMA instructions per wave per stage: X and W row groups, activation
+    // scales, and (per-row weight scales) the W-row scales
+    static constexpr int DPW = XG + WG + 1 + (WROW_ ? 1 : 0);
+    // per-row weight scales: a ring of STAGES + 1 slots after the stages, so
+    // that the slot a step reads is never the one being refilled while the
+    // step still rescales (the refill of step s + STAGES, issued during step s,
+    // goes to the slot of step s - 1).  A slot gives each wave 256 bytes: the
+    // first BN / 64 waves fetch the BN scales, the others issue the same
+    // instruction on an empty range into their own, unread, quarter.
+    static constexpr int WSR_SLOTS = WROW_ ? STAGES_ + 1 : 0;
+    static constexpr int WSR_STRIDE = NW * 256;
+    static constexpr int WSR_OFF = STAGES_ * STAGE_BYTES;
+    static constexpr int WSR_BYTES = WSR_SLOTS * WSR_STRIDE;
+    static_assert(!WROW_ || BN <= NW * 64, "one W-row scale per lane of the first BN / 64 waves");
     static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "row groups must split evenly over the waves");
     static_assert(BM % 16 == 0, "16-row layout groups must not straddle X and W");
@@ -475,10 +488,11 @@ struct DmaCfg {
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must lie in one 128-wide weight scale block");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
     // output staging: 64 bf16 columns per row where they fit, else 32
-    static constexpr int EPI_CW = STAGES * STAGE_BYTES + NW * 16 * (64 * 2 + 16) <= 160 * 1024 ? 64 : 32;
+    static constexpr int EPI_CW = STAGES * STAGE_BYTES + WSR_BYTES + NW * 16 * (64 * 2 + 16) <= 160 * 1024 ? 64 : 32;
     static constexpr int EPI_RS = EPI_CW * 2 + 16;
     static constexpr int EPI_BYTES = NW * 16 * EPI_RS;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + EPI_BYTES;
+    static constexpr int EPI_OFF = STAGES * STAGE_BYTES + WSR_BYTES;
+    static constexpr int LDS_BYTES = EPI_OFF + EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU (stages and output staging)");
     static_assert(WN % EPI_CW == 0 && EPI_BYTES % 1024 == 0, "output staging chunks");
 };
@@ -586,15 +600,24 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, T
 // article's closing section), so each K block's scale product 2^e is exact
 // and goes to the MFMA's E8M0 scale operand: the matrix core accumulates
 // 2^e * P into the accumulator itself and the fp32 VALU rescale disappears.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT, bool POW2>
+// WROW: per-row weight scales ws [N, K/128] (the weight gradient, whose both
+// operands are quantized in 1x128 blocks along the tokens): each K step's BN
+// W-row scales travel with its operands into a ring of LDS slots, and the
+// rescale forms xs * ws for each lane's 4 columns of a tile.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT, bool POW2,
+          bool WROW = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs args)
 {
+    static_assert(!(WROW && (POW2 || GROUPED)), "per-row weight scales: dense products, VALU rescale");
     GemmArgs a = args;
     if constexpr (GROUPED)
         a.tiles_m = *(const CONST_AS int32_t *)a.gcount; // the tiles that exist
-    // three LDS stages (two steps of loads in flight) where they fit
-    constexpr int NST = 3 * DmaCfg<BM, BN, WAVES_M, WAVES_N, 2>::STAGE_BYTES <= 160 * 1024 ? 3 : 2;
-    using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, NST>;
+    // three LDS stages (two steps of loads in flight) where they fit beside
+    // the W-row scale ring and the narrower output staging
+    using C2 = DmaCfg<BM, BN, WAVES_M, WAVES_N, 2, WROW>;
+    constexpr int NST =
+        3 * C2::STAGE_BYTES + (WROW ? 4 * C2::WSR_STRIDE : 0) + C2::NW * 16 * (32 * 2 + 16) <= 160 * 1024 ? 3 : 2;
+    using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, NST, WROW>;
     // one array: the operand stages, then the output staging area (two
     // separate __shared__ arrays made the main loop run at half speed)
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
@@ -607,7 +630,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     const int ntiles = a.tiles_m * a.tiles_n * (SPLIT ? a.ksplit : 1); // work units
     const int sub = lane >> 3, slot = lane & 7;
     const int fr = lane & 15, fg = lane >> 4;
-    uint8_t *const epi_lds = lds + C::STAGES * C::STAGE_BYTES + wave * 16 * C::EPI_RS; // this wave's staging rows
+    uint8_t *const epi_lds = lds + C::EPI_OFF + wave * 16 * C::EPI_RS; // this wave's staging rows
 
     // ---- DMA cursor: the tile and K block whose operands load next ----
     int dv = blockIdx.x;
@@ -637,6 +660,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // resources)
     const uint8_t *xbase, *wbase;
     const float *sbase;
+    const float *wrbase = nullptr; // WROW: the tile's W-row scales (rows n0 .. n0 + BN - 1)
     uint32_t xnr[C::XG]; // bytes of X in row group t (0 past the tile's last row)
     uint32_t snr;        // bytes of the tile's activation-scale rows
     const int r0 = tile_row(wave * 8 + sub);
@@ -646,6 +670,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         xbase = a.xq + g.row_begin * K;
         wbase = g.wq + g.n0 * K;
         sbase = a.xs + g.row_begin * KB;
+        if constexpr (WROW)
+            wrbase = g.ws + g.n0 * KB;
         const int64_t rows = g.row_end - g.row_begin; // 1 .. BM
 #pragma unroll
         for (int t = 0; t < C::XG; ++t) {
@@ -659,9 +685,21 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // range is empty, so the same instructions move nothing (the hardware
     // range check drops them): the caller issues them unconditionally,
     // keeping the MFMA stream they sit in free of branches.
-    auto issue_q = [&](int q, int64_t kb, int stage, bool live) __attribute__((always_inline)) {
+    auto issue_q = [&](int q, int64_t kb, int stage, int wslot, bool live) __attribute__((always_inline)) {
         uint8_t *L = lds + stage * C::STAGE_BYTES;
         const int ko = (int)(kb * BK);
+        if (WROW && q == C::XG + C::WG + 1) {
+            // W-row scales of K block kb: lane l of wave w < BN / 64 fetches row
+            // 64 w + l into its quarter of slot `wslot`; the other waves issue
+            // on an empty range into their own quarters, which nothing reads
+            const bool mine = wave < BN / 64;
+            const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(wrbase), (short)0, (live && mine) ? (int)(BN * KB * 4) : 0, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (LDS_AS void *)(lds + C::WSR_OFF + wslot * C::WSR_STRIDE + wave * 256), 4,
+                (int)((uint32_t)((mine ? wave * 64 + lane : 0) * KB * 4)), (int)(kb * 4), 0, 0);
+            return;
+        }
         if (q < C::XG) {
             const int t = q;
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -682,9 +720,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         }
     };
     auto issue = [&](int64_t kb, int stage, bool live = true) {
+        // (the prologue's steps 0 .. STAGES - 1 use W-row slots 0 .. STAGES - 1)
 #pragma unroll
         for (int q = 0; q < C::DPW; ++q)
-            issue_q(q, kb, stage, live);
+            issue_q(q, kb, stage, stage, live);
     };
     // advance the DMA cursor by one K block; false at the end of the stream
     auto dma_next = [&]() {
@@ -742,9 +781,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
+    // WROW: this lane's 4 W-row scales of n-tile j, in slot j % 2 (read at the
+    // start of group j; group j's last rescale runs in group j + 1)
+    v4f wsv[2];
     auto rescale = [&](int t, const v4f &p) {
         const int i = t % C::TM, j = t / C::TM;
-        acc[i][j] = __builtin_elementwise_fma(v4f{sc[i], sc[i], sc[i], sc[i]}, p, acc[i][j]);
+        if constexpr (WROW)
+            acc[i][j] = __builtin_elementwise_fma(v4f{sc[i], sc[i], sc[i], sc[i]} * wsv[j & 1], p, acc[i][j]);
+        else
+            acc[i][j] = __builtin_elementwise_fma(v4f{sc[i], sc[i], sc[i], sc[i]}, p, acc[i][j]);
     };
     static_assert(C::TN >= 4, "the W-fragment ring needs at least four groups per step");
 
@@ -765,10 +810,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // fragment registers for the next step's.  (For the last step of a
     // workgroup those reads fetch data that is never used; the barrier is
     // uniform.)
-    auto compute = [&](int stage, int nstage, bool full_wait, const CONST_AS float *swp, auto &&load_q)
+    auto compute = [&](int stage, int nstage, int wcur, bool full_wait, const CONST_AS float *swp, auto &&load_q)
                        __attribute__((always_inline)) {
         const uint8_t *L = lds + stage * C::STAGE_BYTES;
         const uint8_t *Ln = lds + nstage * C::STAGE_BYTES;
+        const uint8_t *Lw = lds + C::WSR_OFF + wcur * C::WSR_STRIDE + (wn * C::WN + 4 * fg) * 4;
         v4f part[2];
         float xs_next[C::TM];
         float sw_next = 0.f;
@@ -785,6 +831,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
             const bool last = j + 1 == C::TN;
+            // (issued before the group's fragment reads: LDS reads complete in
+            // order, so waiting for it leaves those in flight)
+            if constexpr (WROW)
+                wsv[j & 1] = *(const v4f *)(Lw + j * 64);
             if (j + 2 < C::TN) {
                 awq[(j + 2) % 3] = frag(L + wo[0] + (j + 2) * 2048, L + wo[1] + (j + 2) * 2048);
             } else if (j + 2 == C::TN) {
@@ -803,7 +853,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 // an LDS read falls between here and the end of the step, where
                 // the reads issued below are waited for anyway, so the scalar
                 // load's out-of-order return costs nothing
-                sw_next = *swp;
+                if constexpr (!WROW)
+                    sw_next = *swp;
+                else
+                    sw_next = 1.0f; // (the weight scale is applied per column)
                 awq[(j + 2) % 3] = frag(Ln + wo[0], Ln + wo[1]);
 #pragma unroll
                 for (int i = 0; i < C::TM; ++i)
@@ -953,7 +1006,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     wait_vmcnt<(C::STAGES - 2) * C::DPW>();
     sync();
     {
-        const float sw = ws_of(ct)[ct.kb0];
+        const float sw = WROW ? 1.0f : ws_of(ct)[ct.kb0];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
             sc[i] = *(const float *)(lds + so + i * 64) * sw;
@@ -974,6 +1027,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     }
 
     int stage = 0;
+    int wcur = 0; // W-row scale slot of the step being computed (WROW)
     int64_t ckb = ct.kb0;
     bool advance = false; // the cursor's step was issued during the previous step
     bool stored = false;  // the previous step ended with a tile's output stores
@@ -987,9 +1041,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         // only the loads go in the middle of the MFMA stream; the cursor
         // advances (and sets up the next tile's loads) at the top of the
         // next step
-        compute(stage, nstage, stored, wsp1, [&](int q) { issue_q(q, kbS, stage, hasS); });
+        // step s + STAGES refills the W-row slot of step s - 1
+        const int wslotS = wcur == 0 ? C::STAGES : wcur - 1;
+        compute(stage, nstage, wcur, stored, wsp1, [&](int q) { issue_q(q, kbS, stage, wslotS, hasS); });
         advance = hasS;
         stage = nstage;
+        wcur = wcur == C::STAGES ? 0 : wcur + 1;
         stored = false;
         if (++ckb == ct.kb1) {
             epilogue(ct);
@@ -1299,7 +1356,7 @@ static hipError_t run_simple(GemmArgs a, int grid, bool out_f32, hipStream_t str
 // the 8 XCDs so that the XCD-contiguous unit ranges line up with the dispatch.
 constexpr int kPersistentGrid = 256;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED, bool POW2>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GROUPED, bool POW2, bool WROW = false>
 static hipError_t run_dma_t(GemmArgs a, bool out_f32, hipStream_t stream)
 {
     const dim3 block(WAVES_M * WAVES_N * 64);
@@ -1307,14 +1364,14 @@ static hipError_t run_dma_t(GemmArgs a, bool out_f32, hipStream_t stream)
     const int grid = units < kPersistentGrid ? units : kPersistentGrid;
     if (GROUPED || a.ksplit == 1) {
         if (out_f32)
-            return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED, false, POW2>, dim3(grid), block, 0,
-                          stream, a);
-        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED, false, POW2>, dim3(grid), block, 0,
-                      stream, a);
+            return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, GROUPED, false, POW2, WROW>, dim3(grid),
+                          block, 0, stream, a);
+        return launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, false, GROUPED, false, POW2, WROW>, dim3(grid), block,
+                      0, stream, a);
     }
     if constexpr (!GROUPED) { // (the grouped form is never split)
-        const hipError_t e = launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, true, POW2>, dim3(grid),
-                                    block, 0, stream, a);
+        const hipError_t e = launch(gemm_dma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, true, POW2, WROW>,
+                                    dim3(grid), block, 0, stream, a);
         if (e != hipSuccess)
             return e;
         const int64_t MN = a.M * a.N;
@@ -1442,12 +1499,12 @@ struct Plan {
 // The kernel, tiling and K split of a dense product: a function of the shape
 // (and the measurement overrides) only, shared by the workspace query and
 // the launch.
-static Plan plan_dense(int64_t M, int64_t N, int64_t K)
+static Plan plan_dense(int64_t M, int64_t N, int64_t K, bool row_scaled = false)
 {
     const int fv = forced_variant();
     const int64_t KB = K / BK;
     Plan p = {K_SIMPLE, (int)((M + 127) / 128), (int)(N / 128), 1};
-    if (skinny_ok(M, N, K) && ((fv == V_AUTO && M <= kSkinnyMaxM) || fv == V_SKINNY)) {
+    if (!row_scaled && skinny_ok(M, N, K) && ((fv == V_AUTO && M <= kSkinnyMaxM) || fv == V_SKINNY)) {
         p.kind = K_SKINNY;
         return p;
     }
@@ -1462,6 +1519,8 @@ static Plan plan_dense(int64_t M, int64_t N, int64_t K)
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     int ks = forced_ksplit() ? forced_ksplit() : choose_ksplit(tiles, KB);
     ks = ks < (int)KB ? ks : (int)KB;
+    if (row_scaled)
+        ks = 1; // (its entry point takes no workspace for partial sums)
     // units are counted in int; a split product's partial sums stay addressable
     while (ks > 1 && tiles * ks > (1 << 30))
         --ks;
@@ -1522,9 +1581,14 @@ hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, co
     a.M = M;
     a.N = N;
     a.K = K;
-    a.tiles_m = (int)((M + 127) / 128);
-    a.tiles_n = (int)(N / 128);
+    const Plan p = plan_dense(M, N, K, true);
+    a.tiles_m = p.tiles_m;
+    a.tiles_n = p.tiles_n;
     a.ksplit = 1;
+    if (p.kind == K_DMA256)
+        return run_dma_t<256, 256, 4, 2, false, false, true>(a, out_fp32 != 0, stream);
+    if (p.kind == K_DMA128)
+        return run_dma_t<128, 256, 2, 4, false, false, true>(a, out_fp32 != 0, stream);
     const int grid = a.tiles_m * a.tiles_n;
     const dim3 block(2 * 2 * 64);
     if (out_fp32)

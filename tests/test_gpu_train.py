@@ -200,8 +200,10 @@ def _abs_codes(q):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("shape", [(256, 256, 384), (384, 512, 128), (128, 128, 256), (640, 1152, 384)],
-                         ids=lambda s: "%dx%dx%d" % s)
+@pytest.mark.parametrize("shape", [
+    (256, 256, 384), (384, 512, 128), (640, 1152, 384),       # input width not a multiple of 256: 128x128 kernel
+    (128, 128, 256), (256, 384, 512), (384, 1152, 768),       # the persistent kernel, 128x256 tiles
+], ids=lambda s: "%dx%dx%d" % s)
 def test_wgrad_parity_full_output(fp8bs, orc, shape, mode):
     M, N, K = shape
     say("wgrad tokens=%d N=%d K=%d mode=%d" % (M, N, K, mode))
@@ -211,10 +213,14 @@ def test_wgrad_parity_full_output(fp8bs, orc, shape, mode):
     gemm_gate_abs("dW fp32", host(dw32), ref, abs_sum)
 
 
-@pytest.mark.parametrize("case", DGRAD_LARGE, ids=lambda c: c[0])
+# the weight gradients of the 8B-shaped layers over 8192 tokens (persistent kernel, 256x256 tiles), and
+# one K step per tile with two tiles per workgroup (the W-row scale slots wrap across tile changes)
+WGRAD_LARGE = [(n, N, K, 8192) for n, N, K in DGRAD_LARGE] + [("tokens128_many_tiles", 8192, 4096, 128)]
+
+
+@pytest.mark.parametrize("case", WGRAD_LARGE, ids=lambda c: c[0])
 def test_wgrad_parity_full_size_sampled(fp8bs, orc, case):
-    name, N, K = case
-    M = 8192
+    name, N, K, M = case
     say("wgrad %s tokens=%d N=%d K=%d" % (name, M, N, K))
     dw32, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, 0)
     rows, cols = sample_positions(N, K, 3000, seed=M + N + K)
