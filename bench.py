@@ -370,15 +370,15 @@ def decode_workload(fp8bs, dev, mode):
     pairs = []
     for wname, N, K in (("gate_up", 28672, 4096), ("down", 4096, 14336)):
         log("generating %s weights [%d, %d]" % (wname, N, K))
-        # five weight copies rotated over the steps, so that the 256 MB
+        # five weight copies rotated over the calls, so that the 256 MB
         # infinity cache never holds the weights a GEMM reads
         copies = []
         for c in range(5):
             wq, ws = fp8bs.quant_w_128x128(bf16_dev(synth.weights(N, K, sub=synth.sub_layer(40 + c)), dev), mode)
             copies.append((wq, ws))
-        for M in (1, 16, 64, 256):
+        for j, M in enumerate((1, 16, 64, 256)):
             x = bf16_dev(synth.activations(M, K, sub=synth.SUB_X + M), dev)
-            pairs.append(dict(name="%s_m%d" % (wname, M), M=M, N=N, K=K, x=x, copies=copies,
+            pairs.append(dict(name="%s_m%d" % (wname, M), M=M, N=N, K=K, x=x, copies=copies, j=j,
                               xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
                               xs=torch.empty((M, K // 128), dtype=torch.float32, device=dev),
                               y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
@@ -390,11 +390,14 @@ def decode_workload(fp8bs, dev, mode):
 
     def step(timer):
         # the linear layer from bf16 activations: one launch for M <= 16 (X
-        # quantized inside the weight-streaming GEMM), quantizer + GEMM above
-        c = it[0] % 5
+        # quantized inside the weight-streaming GEMM or the one-row GEMV),
+        # quantizer + GEMM above.  Each call of a step reads its own weight
+        # copy: between two reads of a copy, more than the 256 MB cache's
+        # worth of other weights passes
+        c = it[0]
         it[0] += 1
         for p in pairs:
-            wq, ws = p["copies"][c]
+            wq, ws = p["copies"][(c + p["j"]) % 5]
             maybe(timer, "linear_" + p["name"],
                   lambda p=p, wq=wq, ws=ws: linear(p["x"], wq, ws, out=p["y"], workspace=p["lin_buf"]))
 
@@ -402,7 +405,7 @@ def decode_workload(fp8bs, dev, mode):
         # the same layer as two separate calls, timed apart (reported beside the step)
         for r in range(reps):
             for p in pairs:
-                wq, ws = p["copies"][r % 5]
+                wq, ws = p["copies"][(r + p["j"]) % 5]
                 maybe(timer, "quant_" + p["name"],
                       lambda p=p: fp8bs.quant_act_1x128(p["x"], mode, out=(p["xq"], p["xs"])))
                 maybe(timer, "gemm_" + p["name"],

@@ -299,6 +299,10 @@ static int gemm_impl(const void *xq, const float *xs, const void *wq, const floa
         return FP8BS_INVALID_ARG;
     if ((st = check_device()) != FP8BS_OK)
         return st;
+    // one activation row: the weight-streaming GEMV (any scales; it takes no workspace)
+    if (fp8bs::gemv_ok(M, N, K))
+        return status_of(fp8bs::launch_gemv(xq, xs, wq, ws, N, K, y, out_dtype == FP8BS_OUT_FP32, 0,
+                                            (hipStream_t)stream));
     return status_of(fp8bs::launch_gemm(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, pow2, workspace,
                                         (hipStream_t)stream));
 }
@@ -359,6 +363,10 @@ static int linear_impl(const void *x, const void *wq, const float *ws, int64_t M
         return FP8BS_INVALID_ARG;
     if ((st = check_device()) != FP8BS_OK)
         return st;
+    // one activation row: the GEMV quantizes it in-kernel (the workspace goes unused)
+    if (fp8bs::gemv_ok(M, N, K))
+        return status_of(fp8bs::launch_gemv(x, nullptr, wq, ws, N, K, y, out_dtype == FP8BS_OUT_FP32, pow2 ? 2 : 1,
+                                            (hipStream_t)stream));
     return status_of(fp8bs::launch_linear(x, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, pow2, workspace,
                                           (hipStream_t)stream));
 }

@@ -66,6 +66,13 @@ hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, co
 size_t linear_workspace_size(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(const void *x, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K, void *y,
                          int out_fp32, int pow2, void *workspace, hipStream_t stream);
+// One activation row on the vector ALUs (fp8bs_gemv.hip): gemv_ok says
+// whether the product qualifies (M == 1, K <= 16384); quantize 0 takes codes
+// and scales, 1 / 2 bf16 activations quantized in-kernel (EXACT / POW2), with
+// the codes and scale quant_act_1x128 writes.  No workspace.
+bool gemv_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(const void *x, const float *xs, const void *wq, const float *ws, int64_t N, int64_t K, void *y,
+                       int out_fp32, int quantize, hipStream_t stream);
 size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,

@@ -61,6 +61,8 @@ SMALL = [
     (40, 512, 8192), (97, 512, 2944), (300, 512, 4096),
     # a few rows with K past the weight-streaming kernel's 16384: the persistent kernel, 32 K ranges
     (3, 256, 32768),
+    # one activation row (the vector-ALU GEMV): all 16 K chunks, a partial last chunk, past its K limit
+    (1, 512, 16384), (1, 384, 640), (1, 256, 16512),
 ]
 
 
@@ -125,7 +127,7 @@ def test_gemm_empty(fp8bs):
 LARGE = [
     ("qkv", 8192, 6144, 4096), ("gate_up", 8192, 28672, 4096), ("down", 8192, 4096, 14336),
     ("o_proj", 8192, 4096, 4096),
-    ("decode1_gate_up", 1, 28672, 4096), ("decode16_down", 16, 4096, 14336),
+    ("decode1_gate_up", 1, 28672, 4096), ("decode1_down", 1, 4096, 14336), ("decode16_down", 16, 4096, 14336),
     ("decode64_gate_up", 64, 28672, 4096), ("decode256_down", 256, 4096, 14336),
     # one K block per tile and more tiles than workgroups: every workgroup walks several one-step tiles
     ("k128_many_tiles", 4352, 4096, 128),

@@ -1,8 +1,9 @@
 """GPU parity of the whole linear layer from bf16 activations (fp8_block_linear).
 
-The entry point quantizes X per 1x128 block and multiplies: for decode rows
-(M <= 16, 8 <= K/128 <= 128) inside the weight-streaming GEMM, elsewhere
-through the quantizer and the GEMM.  Gates, on the same seeded bf16 inputs:
+The entry point quantizes X per 1x128 block and multiplies: for one row
+(M = 1, K <= 16384) inside the vector-ALU GEMV, for other decode rows
+(M <= 16, 8 <= K/128 <= 128, W tiles of 32 or 64 rows) inside the
+weight-streaming GEMM, elsewhere through the quantizer and the GEMM.  Gates, on the same seeded bf16 inputs:
 - against the oracle's own composition, its quant_act_1x128 then its GEMM:
   max |Y_gpu - Y_oracle| <= 1e-2 * rms(Y_oracle) on the fp32 output;
 - bf16 output == round-to-nearest-even of the fp32 output, bit for bit;
@@ -37,6 +38,8 @@ UNFUSED = [
     # 16-row W tiles (N/32 < 256), more rows, too few K blocks for the weight-streaming kernel, or too many
     (16, 4096, 14336), (5, 512, 2048), (1, 256, 1024), (17, 4096, 4096), (256, 512, 512), (16, 256, 512),
     (3, 256, 32768), (300, 512, 4096),
+    # one row: the GEMV quantizes it in-kernel whatever the workspace query says
+    (1, 4096, 14336), (1, 512, 640),
 ]
 
 
