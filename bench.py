@@ -223,11 +223,11 @@ def train_workload(fp8bs, dev, mode):
         # the step's recalibration for training: W and W^T codes from one read of each weight
         maybe(timer, "quant_w_all", lambda: fp8bs.quant_w_128x128_dual_batched(w_all, mode, outs=out_all))
         for b in bufs:
-            maybe(timer, "quant_act_" + b["name"],
-                  lambda: fp8bs.quant_act_1x128(b["dy"], mode, out=(b["dyq"], b["dys"])))
+            # dY quantized along its rows (data gradient) and along the tokens (weight gradient), one read
+            maybe(timer, "quant_act_dual_dy_" + b["name"],
+                  lambda: fp8bs.quant_act_1x128_dual(b["dy"], mode, out=(b["dyq"], b["dys"]) + b["dyt"]))
             maybe(timer, "gemm_" + b["name"],
                   lambda: gemm(b["dyq"], b["dys"], b["outs"][2], b["outs"][3], out=b["dx"]))
-            maybe(timer, "quant_act_t_dy_" + b["name"], lambda: fp8bs.quant_act_1x128_t(b["dy"], mode, out=b["dyt"]))
             maybe(timer, "quant_act_t_x_" + b["name"], lambda: fp8bs.quant_act_1x128_t(b["x"], mode, out=b["xt"]))
             maybe(timer, "wgrad_" + b["name"],
                   lambda: fp8bs.fp8_block_gemm_1x128(b["dyt"][0], b["dyt"][1], b["xt"][0], b["xt"][1], out=b["dw"]))
@@ -249,9 +249,11 @@ def summarize_train(bufs, timer):
         kernels["wgrad_" + b["name"]] = mfma_entry(t, 2.0 * M * N * K)
         w_ms.append(t)
         w_flops.append(2.0 * M * N * K)
-        for what, width in (("dy", K), ("x", N)):
-            kernels["quant_act_t_%s_%s" % (what, b["name"])] = hbm_entry(
-                timer.avg_ms("quant_act_t_%s_%s" % (what, b["name"])), M * width * 3 + (M * width // 128) * 4)
+        # dY [M, K] (K = the forward N here): bf16 read once, two code sets and two scale sets written
+        kernels["quant_act_dual_dy_" + b["name"]] = hbm_entry(
+            timer.avg_ms("quant_act_dual_dy_" + b["name"]), M * K * 4 + (M * K // 128) * 8)
+        kernels["quant_act_t_x_" + b["name"]] = hbm_entry(
+            timer.avg_ms("quant_act_t_x_" + b["name"]), M * N * 3 + (M * N // 128) * 4)
     d_ms = roof["avg_launch_ms"] * len(bufs)
     if sum(w_ms) > d_ms:
         mean_ms, mean_flops = sum(w_ms) / len(w_ms), sum(w_flops) / len(w_flops)
@@ -274,8 +276,9 @@ def summarize_dense(bufs, timer, dual=False):
         kernels["gemm_" + b["name"]] = mfma_entry(t, 2.0 * M * N * K)
         gemm_ms.append(t)
         gemm_flops.append(2.0 * M * N * K)
-        kernels["quant_act_" + b["name"]] = hbm_entry(timer.avg_ms("quant_act_" + b["name"]),
-                                                      M * K * 3 + (M * K // 128) * 4)
+        if "quant_act_" + b["name"] in timer.pairs:
+            kernels["quant_act_" + b["name"]] = hbm_entry(timer.avg_ms("quant_act_" + b["name"]),
+                                                          M * K * 3 + (M * K // 128) * 4)
     # bf16 read, codes written (twice for the dual form: W and W^T), one fp32 per block (twice)
     wb = 4 if dual else 3
     kernels["quant_w_all"] = hbm_entry(timer.avg_ms("quant_w_all"),
@@ -573,8 +576,8 @@ def main():
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "training backward of the 8B-shaped dense layer at M=8192 tokens: "
                                       "recalibrate 4 weights to W and W^T codes (one batched launch); per layer "
-                                      "quantize dY (1x128 along N), data-gradient GEMM dX = dY W, quantize dY^T "
-                                      "and X^T (1x128 along the tokens), weight-gradient GEMM dW = dY^T X; "
+                                      "quantize dY along N and along the tokens (one read), data-gradient GEMM "
+                                      "dX = dY W, quantize X^T along the tokens, weight-gradient GEMM dW = dY^T X; "
                                       "QKV, gate+up, down, o_proj",
                           "scale_mode": "pow2" if args.mode else "exact", "out_dtype": "bf16",
                           "gemm_flops_per_step": flops},

@@ -34,6 +34,7 @@ OUT_FP32 = 1
 EXPORTS = (
     "quant_act_1x128",
     "quant_act_1x128_t",
+    "quant_act_1x128_dual",
     "quant_w_128x128",
     "quant_w_128x128_batched",
     "quant_w_128x128_dual",
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         L.quant_act_1x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_act_1x128_t.argtypes = [P, I64, I64, P, P, I32, P]
+        L.quant_act_1x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
         L.fp8_block_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
@@ -91,7 +93,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.argtypes = [I32]
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
-        for fn in ("quant_act_1x128", "quant_act_1x128_t", "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
+        for fn in ("quant_act_1x128", "quant_act_1x128_t", "quant_act_1x128_dual", "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
@@ -175,6 +177,24 @@ def quant_act_1x128_t(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
         xqt, xst = out
     _check("quant_act_1x128_t", lib().quant_act_1x128_t(_ptr(x), M, K, _ptr(xqt), _ptr(xst), int(mode), _stream(x)))
     return xqt, xst
+
+
+def quant_act_1x128_dual(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 [M, K] -> (xq [M, K], xs [M, K/128], xqt [K, M], xst [K, M/128]): quant_act_1x128
+    of X and of X^T from one read of X."""
+    x = _bf16_payload(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.uint8, device=x.device),
+               torch.empty((M, K // 128), dtype=torch.float32, device=x.device),
+               torch.empty((K, M), dtype=torch.uint8, device=x.device),
+               torch.empty((K, M // 128), dtype=torch.float32, device=x.device))
+    xq, xs, xqt, xst = out
+    _check("quant_act_1x128_dual", lib().quant_act_1x128_dual(_ptr(x), M, K, _ptr(xq), _ptr(xs), _ptr(xqt),
+                                                              _ptr(xst), int(mode), _stream(x)))
+    return xq, xs, xqt, xst
 
 
 def quant_w_128x128(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):

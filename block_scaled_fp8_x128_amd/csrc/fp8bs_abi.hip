@@ -143,6 +143,26 @@ int quant_act_1x128_t(const void *x_bf16, int64_t M, int64_t K, void *xqt, float
     return status_of(fp8bs::launch_quant_act_t(x_bf16, M, K, xqt, xst, scale_mode, (hipStream_t)stream));
 }
 
+int quant_act_1x128_dual(const void *x_bf16, int64_t M, int64_t K, void *xq, float *xs, void *xqt, float *xst,
+                         int scale_mode, void *stream)
+{
+    if (M < 0 || K <= 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))
+        return FP8BS_INVALID_ARG;
+    if (M % 128 != 0 || K % 128 != 0 || (M / 128) * (K / 128) >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (M == 0)
+        return FP8BS_OK;
+    int st = check_quant(x_bf16, M, K, xq, xs, scale_mode, false);
+    if (st != FP8BS_OK)
+        return st;
+    if (!tensor_ok(xqt, M * K, 16) || !tensor_ok(xst, M * K, 4))
+        return FP8BS_INVALID_ARG;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(
+        fp8bs::launch_quant_act_t(x_bf16, M, K, xqt, xst, scale_mode, (hipStream_t)stream, xq, xs));
+}
+
 int quant_w_128x128(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, int scale_mode, void *stream)
 {
     int st = check_quant(w_bf16, N, K, wq, ws, scale_mode, true);

@@ -30,9 +30,11 @@ static inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, s
 // ---- quantizers (fp8bs_quant.hip) ------------------------------------------
 
 hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float *xs, int mode, hipStream_t stream);
-// quant_act_1x128 of X^T: codes [K, M], scales [K, M/128] (M, K multiples of 128).
+// quant_act_1x128 of X^T: codes [K, M], scales [K, M/128] (M, K multiples of
+// 128); with xq != nullptr also quant_act_1x128 of X itself (xq [M, K], xs
+// [M, K/128]) from the same read.
 hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, float *xst, int mode,
-                              hipStream_t stream);
+                              hipStream_t stream, void *xq = nullptr, float *xs = nullptr);
 
 // One weight tensor of a batched weight quantization (qt, st: the transposed
 // codes [K, N] and scales [K/128, N/128], written by the dual launcher only).

@@ -374,9 +374,15 @@ hipError_t launch_quant_w_dual(const WTensor *t, int64_t count, int mode, hipStr
 // row or a piece index hit different banks).  The tile's 128 rows of X^T are
 // then 1x128 blocks, quantized exactly as quant_act_kernel does: a 16-lane
 // DPP row per block, one 16-byte chunk per lane.
-template <int MODE>
+// ROWS: also the ordinary 1x128 quantization of X (codes [M, K], scales
+// [M, K/128]) from the same read.  Each row of the tile is one block whose
+// 128 values sit in the 16 consecutive lanes that share 8 rows, so it is the
+// activation quantizer's 16-lane block once more, before the transpose.
+template <int MODE, bool ROWS = false>
 __global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
-                                                                 float *__restrict__ s, int64_t M, int64_t K)
+                                                                 float *__restrict__ s, int64_t M, int64_t K,
+                                                                 uint8_t *__restrict__ qr = nullptr,
+                                                                 float *__restrict__ sr = nullptr)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tl[128 * 256]; // the transposed bf16 tile
     const int64_t KB = K / 128, MB = M / 128;
@@ -389,6 +395,16 @@ __global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t 
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         v[j] = __builtin_nontemporal_load((const u32x4 *)(x + base + j * K));
+    if constexpr (ROWS) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            BlockQuant<MODE> bq;
+            bq.init(amax_value(row16_max(chunk_max_mag(v[j]))));
+            __builtin_nontemporal_store(quant_chunk<MODE>(v[j], bq), (u32x2 *)(qr + base + j * K));
+            if (c == 0)
+                sr[(mb * 128 + 8 * rg + j) * KB + kb] = bq.s;
+        }
+    }
     // transposed row i (column 8 c + i of the tile) holds element i of rows
     // 8 rg .. 8 rg + 7; its dword p pairs rows 2p (low half) and 2p + 1
 #pragma unroll
@@ -422,16 +438,22 @@ __global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t 
 }
 
 hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, float *xst, int mode,
-                              hipStream_t stream)
+                              hipStream_t stream, void *xq, float *xs)
 {
     const int64_t tiles = (M / 128) * (K / 128);
     if (tiles == 0)
         return hipSuccess;
+    const dim3 g((unsigned)tiles), b(QW_THREADS);
+    const uint16_t *xp = (const uint16_t *)x;
+    uint8_t *qt = (uint8_t *)xqt, *qr = (uint8_t *)xq;
+    if (xq != nullptr) {
+        if (mode == SCALE_POW2)
+            return launch(quant_act_t_kernel<SCALE_POW2, true>, g, b, 0, stream, xp, qt, xst, M, K, qr, xs);
+        return launch(quant_act_t_kernel<SCALE_EXACT, true>, g, b, 0, stream, xp, qt, xst, M, K, qr, xs);
+    }
     if (mode == SCALE_POW2)
-        return launch(quant_act_t_kernel<SCALE_POW2>, dim3((unsigned)tiles), dim3(QW_THREADS), 0, stream,
-                      (const uint16_t *)x, (uint8_t *)xqt, xst, M, K);
-    return launch(quant_act_t_kernel<SCALE_EXACT>, dim3((unsigned)tiles), dim3(QW_THREADS), 0, stream,
-                  (const uint16_t *)x, (uint8_t *)xqt, xst, M, K);
+        return launch(quant_act_t_kernel<SCALE_POW2, false>, g, b, 0, stream, xp, qt, xst, M, K, qr, xs);
+    return launch(quant_act_t_kernel<SCALE_EXACT, false>, g, b, 0, stream, xp, qt, xst, M, K, qr, xs);
 }
 
 } // namespace fp8bs

@@ -115,6 +115,18 @@ FP8BS_API int quant_act_1x128_t(const void *x_bf16, int64_t M, int64_t K, void *
                                 void *stream);
 
 /*
+ * quant_act_1x128_dual -- quant_act_1x128 and quant_act_1x128_t of the same
+ * X [M, K] from one read of X: (xq [M, K], xs [M, K/128]) exactly as
+ * quant_act_1x128 writes them, and (xqt [K, M], xst [K, M/128]) exactly as
+ * quant_act_1x128_t does.  A training step quantizes each output gradient
+ * dY both ways: along its rows for the data gradient dX = dY W, along the
+ * tokens for the weight gradient dW = dY^T X.  Errors: as quant_act_1x128_t,
+ * and INVALID_ARG for a null or misaligned output.  M == 0 is a no-op.
+ */
+FP8BS_API int quant_act_1x128_dual(const void *x_bf16, int64_t M, int64_t K, void *xq, float *xs, void *xqt,
+                                   float *xst, int scale_mode, void *stream);
+
+/*
  * quant_w_128x128 -- weight quantizer, one scale per 128x128 block (article
  * section "Technical breakthrough": 128x128 granularity for weights).  Called
  * on every weight after each optimizer step, it is the per-step scale

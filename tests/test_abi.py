@@ -140,6 +140,12 @@ def test_weight_gradient_entry_validation(fp8bs):
     assert q(FAKE, 128, 128, NULL, FAKE, 0, NULL) == 1     # null codes
     assert q(MISAL, 128, 128, FAKE, FAKE, 0, NULL) == 1    # misaligned input
     assert q(NULL, 0, 128, NULL, NULL, 0, NULL) == 0       # M == 0: no-op
+    d = L.quant_act_1x128_dual
+    assert d(FAKE, 100, 128, FAKE, FAKE, FAKE, FAKE, 0, NULL) == 2     # M % 128
+    assert d(FAKE, 128, 128, FAKE, FAKE, NULL, FAKE, 0, NULL) == 1     # null transposed codes
+    assert d(FAKE, 128, 128, NULL, FAKE, FAKE, FAKE, 0, NULL) == 1     # null row codes
+    assert d(FAKE, 128, 128, FAKE, FAKE, MISAL, FAKE, 0, NULL) == 1    # misaligned transposed codes
+    assert d(NULL, 0, 128, NULL, NULL, NULL, NULL, 1, NULL) == 0       # M == 0: no-op
     g = L.fp8_block_gemm_1x128
     assert g(FAKE, FAKE, FAKE, FAKE, 8, 100, 128, FAKE, 0, NULL) == 2   # N % 128
     assert g(FAKE, FAKE, FAKE, FAKE, 8, 128, 100, FAKE, 0, NULL) == 2   # K % 128

@@ -146,6 +146,23 @@ def test_quant_act_t_parity(fp8bs, orc, shape, mode):
     assert_bitexact("scales", host(s), s_ref)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", [(128, 128), (384, 1152), (8192, 4096), (8192, 28672)], ids=lambda s: "%dx%d" % s)
+def test_quant_act_dual_parity(fp8bs, orc, shape, mode):
+    """Both quantizations of an output gradient from one read: bit-exact against the
+    oracle's quant_act_1x128 of dY and of dY^T."""
+    M, K = shape
+    say("quant_act_1x128_dual M=%d K=%d mode=%d" % (M, K, mode))
+    dy = synth.activations(M, K, seed=synth.SEED, sub=synth.SUB_DY)
+    xq, xs, xqt, xst = fp8bs.quant_act_1x128_dual(bf16_to_dev(dy), mode)
+    q_ref, s_ref = orc.quant_act_1x128(dy, mode)
+    assert_bitexact("row codes", host(xq), q_ref)
+    assert_bitexact("row scales", host(xs), s_ref)
+    qt_ref, st_ref = orc.quant_act_1x128_t(dy, mode)
+    assert_bitexact("transposed codes", host(xqt), qt_ref)
+    assert_bitexact("transposed scales", host(xst), st_ref)
+
+
 def _wgrad(fp8bs, orc, M, N, K, mode):
     """dW [N, K] = dY [M, N]^T X [M, K] over M tokens."""
     dy = synth.activations(M, N, seed=synth.SEED, sub=synth.SUB_DY)
