@@ -201,10 +201,14 @@ FP8BS_API int quant_w_128x128_dual_batched(int64_t count, const void *const *w_b
  *   Y[m, n] = sum_kb (xs[m, kb] * ws[n/128, kb]) * P[m, n, kb],
  *   P[m, n, kb] = sum_{k in block kb} decode(xq[m, k]) * decode(wq[n, k]),
  * where P comes from FP8 matrix-core products accumulated in fp32 and the
- * scale product is formed and applied in fp32 per 128-wide K block.  The
- * order of the fp32 additions is the hardware's, so results agree with an
- * exact evaluation to within fp32 rounding, not bit for bit; the bf16 output
- * is the round-to-nearest-even of exactly the value the fp32 output holds.
+ * scale product is formed and applied in fp32 per 128-wide K block (for a
+ * single row, M == 1 with K <= 16384, the products and sums run on the
+ * vector ALUs in fp32 instead).  The order of the additions is the
+ * hardware's, and the matrix cores sum a K block's 128 products at reduced
+ * precision when one product dominates (below 2^-12 of the block's sum of
+ * |products| in every measured case), so results agree with an exact
+ * evaluation closely, not bit for bit; the bf16 output is the
+ * round-to-nearest-even of exactly the value the fp32 output holds.
  * A given (M, N, K) always runs the same kernel: results are deterministic.
  *
  *   workspace, workspace_bytes: device scratch for the fp32 partial sums of
@@ -303,18 +307,20 @@ FP8BS_API int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const
  *   x [M, K] bf16 payloads, row-major
  *   wq, ws, y, out_dtype: as fp8_block_gemm
  *
- * For at most 16 rows (decode) with 8 <= K/128 <= 128 and N a multiple of 32
- * with N/32 >= 256, one kernel reads x, quantizes each 1x128 block in
- * registers with the quantizer's own encoder and multiplies, so no quantized
- * copy of x is written or read back.  Other shapes run quant_act_1x128 into
- * the workspace, then the GEMM.  Either way
+ * For one row (M == 1, K <= 16384) the vector-ALU product for single
+ * activation rows quantizes x in registers; for at most 16 rows (decode) with
+ * 8 <= K/128 <= 128 and N a multiple of 32 with N/32 >= 256, the
+ * weight-streaming kernel does.  Either one uses the quantizer's own encoder,
+ * so no quantized copy of x is written or read back.  Other shapes run
+ * quant_act_1x128 into the workspace, then the GEMM.  Either way
  * y is bit for bit that of quant_act_1x128 followed by fp8_block_gemm (or the
  * _pow2 pair) on the same stream, with the default kernel selection (no
  * FP8BS_GEMM_VARIANT override).
  *
  * Workspace: fp8bs_linear_workspace_size(M, N, K) bytes (0 for the fused
  *   shapes, where workspace may be NULL): the quantized x, its scales, then
- *   the GEMM's own workspace, each 16-byte aligned.  It need not be zeroed;
+ *   the GEMM's own workspace, each 16-byte aligned.  (At M == 1 the size is
+ *   still required, though the single-row product leaves it unused.)  It need not be zeroed;
  *   calls that share a workspace must not overlap in time.
  * Errors: as fp8_block_gemm (x takes xq's place), plus UNSUPPORTED_SHAPE for
  *   shapes quant_act_1x128 rejects.
