@@ -98,6 +98,13 @@ class KernelTimer:
         ps = self.pairs[name]
         return sum(a.elapsed_time(b) for a, b in ps) / len(ps)
 
+    def spread(self, name):
+        """(median, min) of the timed launches of `name`, in ms."""
+        v = sorted(a.elapsed_time(b) for a, b in self.pairs[name])
+        n = len(v)
+        med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+        return med, v[0]
+
     def reset(self):
         self.pairs = {}
 
@@ -656,6 +663,11 @@ def main():
                "kernels": kernels}
         cpu = None
 
+    # median and min beside each per-kernel mean (entries keyed by their timer name)
+    for k, v in out.get("kernels", {}).items():
+        if isinstance(v, dict) and k in timer.pairs:
+            med, mn = timer.spread(k)
+            v["median_ms"], v["min_ms"] = round(med, 4), round(mn, 4)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).view(torch.bfloat16)
         dst = torch.empty_like(src)

@@ -81,3 +81,22 @@ def test_traffic_is_withheld_once_the_kernel_source_changed(bench, tmp_path, mon
     value, why = bench.traffic_for("dense")
     assert value is None and why.startswith("stale")
     assert bench.traffic_for("decode") == (None, None)
+
+
+def test_kernel_timer_median_and_min():
+    """Per-kernel median and min of the timed launches (fake events stand in for HIP events)."""
+    import bench
+
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    kt = bench.KernelTimer()
+    kt.pairs["k"] = [(Ev(0.0), Ev(d)) for d in (3.0, 1.0, 2.0, 10.0)]
+    assert kt.avg_ms("k") == 4.0
+    assert kt.spread("k") == (2.5, 1.0)
+    kt.pairs["odd"] = [(Ev(1.0), Ev(1.0 + d)) for d in (5.0, 4.0, 6.0)]
+    assert kt.spread("odd") == (5.0, 4.0)
