@@ -21,8 +21,10 @@
 //     transposing butterfly (10 lane exchanges for 8 rows), and the per-wave
 //     row sums are added over the waves in wave order through LDS.
 // Every reduction has a fixed order, so results are deterministic.  The
-// products and sums are fp32 (no matrix-core accumulation), so the result
-// differs from the matrix-core path only by fp32 rounding.
+// products and sums are plain fp32, with no matrix-core accumulation: the
+// result differs from the matrix-core path by rounding only, and of the two
+// it is the closer to the exact value (the matrix cores sum a K block's
+// products at reduced precision when one of them dominates).
 //
 // QX = 1 / 2: the activation row arrives as bf16 and each 8-lane group
 // quantizes its 128-value block with the 1x128 quantizer's own encoder
