@@ -57,6 +57,10 @@ def lib():
         L.oracle_block_scale.argtypes = [ctypes.c_float, ctypes.c_int]
         L.oracle_quant_act_1x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
         L.oracle_quant_w_128x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
+        L.oracle_bf16_from_double.restype = ctypes.c_uint16
+        L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        L.oracle_swiglu_bf16.argtypes = [P, I64, I64, P]
+        L.oracle_swiglu_quant_1x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
         L.oracle_gemm.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.oracle_gemm_sampled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P]
@@ -128,6 +132,36 @@ def quant_act_1x128(x_bf16, mode: int = SCALE_EXACT):
     q = np.empty((M, K), dtype=np.uint8)
     s = np.empty((M, K // 128), dtype=np.float32)
     lib().oracle_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), int(mode))
+    return q, s
+
+
+def bf16_from_double(v: float) -> int:
+    """Nearest bf16 payload (ties to even) of a double."""
+    return int(lib().oracle_bf16_from_double(float(v)))
+
+
+def swiglu_bf16(gu_bf16) -> np.ndarray:
+    """gu_bf16: uint16 [M, 2F] (gate columns, then up columns) -> h bf16 payloads [M, F],
+    h = RN_bf16((g * sigma(g)) * u) evaluated in fp64."""
+    gu = _c(gu_bf16, np.uint16)
+    M, F2 = gu.shape
+    if F2 % 2:
+        raise ValueError("gu must have an even number of columns")
+    h = np.empty((M, F2 // 2), dtype=np.uint16)
+    lib().oracle_swiglu_bf16(_ptr(gu), M, F2 // 2, _ptr(h))
+    return h
+
+
+def swiglu_quant_1x128(gu_bf16, mode: int = SCALE_EXACT):
+    """The gated activation of gu [M, 2F], then quant_act_1x128: (codes [M, F], scales [M, F/128])."""
+    gu = _c(gu_bf16, np.uint16)
+    M, F2 = gu.shape
+    F = F2 // 2
+    if F2 % 2 or F % 128:
+        raise ValueError("gu must be [M, 2F] with F a multiple of 128")
+    q = np.empty((M, F), dtype=np.uint8)
+    s = np.empty((M, F // 128), dtype=np.float32)
+    lib().oracle_swiglu_quant_1x128(_ptr(gu), M, F, _ptr(q), _ptr(s), int(mode))
     return q, s
 
 

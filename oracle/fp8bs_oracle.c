@@ -41,7 +41,12 @@
  *                        integer special cases, per-expert decomposition;
  *   gemm_1x128         : numpy fp64 matmul of the dequantized operands (row
  *                        scales on both), the block-scaled gemm where the row
- *                        scales are constant over 128 rows, integer case.
+ *                        scales are constant over 128 rows, integer case;
+ *   bf16_from_double   : integer rounding of fp32 bit patterns, torch's
+ *                        float32 -> bfloat16 cast, hand midpoints, subnormal
+ *                        and overflow boundaries;
+ *   swiglu_*           : 50-digit decimal evaluation rounded to bf16 by exact
+ *                        rational arithmetic, closed-form special cases.
  */
 #include <math.h>
 #include <stdint.h>
@@ -172,24 +177,100 @@ static uint32_t quant_element(float x, float s)
 /* Activation quantizer, 1x128 blocks along K.
  * x: bf16 payloads [M, K] row-major.  q: codes [M, K].  s: fp32 [M, K/128].
  * Block (m, kb) = x[m, 128 kb .. 128 kb + 127].  K must be a multiple of 128. */
+static void quant_act_block(const uint16_t *xb, uint8_t *qb, float *sb, int mode)
+{
+    float amax = 0.0f, sc;
+    int k;
+    for (k = 0; k < 128; ++k) {
+        float a = fabsf(bf16_value(xb[k]));
+        if (a > amax)
+            amax = a;
+    }
+    sc = oracle_block_scale(amax, mode);
+    for (k = 0; k < 128; ++k)
+        qb[k] = (uint8_t)quant_element(bf16_value(xb[k]), sc);
+    *sb = sc;
+}
+
 void oracle_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, int mode)
 {
     int64_t KB = K / 128, b;
 #pragma omp parallel for schedule(static)
     for (b = 0; b < M * KB; ++b) {
-        int64_t m = b / KB, kb = b % KB, k;
-        const uint16_t *xb = x + m * K + kb * 128;
-        uint8_t *qb = q + m * K + kb * 128;
-        float amax = 0.0f, sc;
-        for (k = 0; k < 128; ++k) {
-            float a = fabsf(bf16_value(xb[k]));
-            if (a > amax)
-                amax = a;
-        }
-        sc = oracle_block_scale(amax, mode);
+        int64_t m = b / KB, kb = b % KB;
+        quant_act_block(x + m * K + kb * 128, q + m * K + kb * 128, s + m * KB + kb, mode);
+    }
+}
+
+/* ---- the gated activation between the MLP projections ------------------- */
+
+/* Nearest bf16 (ties to the even payload) of a double, as a bf16 payload.
+ * bf16 keeps 8 significant bits over fp32's exponent range: the spacing of
+ * the values in [2^e, 2^(e+1)) is 2^(e-7) for e >= -126, and 2^-133 below
+ * (subnormals).  Rounding past the largest finite value gives infinity. */
+uint16_t oracle_bf16_from_double(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v), r;
+    float f;
+    uint32_t u;
+    int e, qe;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    (void)frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    qe = (e - 1 >= -126) ? (e - 1) - 7 : -133;
+    r = nearbyint(ldexp(a, -qe)); /* the default rounding mode: nearest, ties to even */
+    r = ldexp(r, qe);
+    if (r >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);
+    f = (float)r; /* exact: r has at most 8 significant bits */
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* SiLU-gated linear unit of the MLP, from the gate+up projection's output.
+ * READING: the article's MLP models (Llama 3.1 8B, Qwen3-30B; opening and
+ * "Real-world performance gains" sections) gate their MLP with
+ * h = silu(g) * u, silu(g) = g * sigma(g), sigma the logistic function; the
+ * article names no activation.  Its section "Technical breakthrough" keeps
+ * non-linear functions in BF16, so h is a bf16 tensor: the value computed in
+ * fp64 as (g * sigma(g)) * u with sigma(g) = 1 / (1 + exp(-g)), rounded once
+ * to bf16.  READING: gu [M, 2F] row-major holds the gate values in columns
+ * 0 .. F-1 and the up values in columns F .. 2F-1 of each row.
+ * h: bf16 payloads [M, F]. */
+static uint16_t swiglu_element(uint16_t g_bf16, uint16_t u_bf16)
+{
+    double g = (double)bf16_value(g_bf16), u = (double)bf16_value(u_bf16);
+    double sig = 1.0 / (1.0 + exp(-g));
+    return oracle_bf16_from_double((g * sig) * u);
+}
+
+void oracle_swiglu_bf16(const uint16_t *gu, int64_t M, int64_t F, uint16_t *h)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M * F; ++i) {
+        int64_t m = i / F, f = i % F;
+        h[i] = swiglu_element(gu[m * 2 * F + f], gu[m * 2 * F + F + f]);
+    }
+}
+
+/* The gated activation, then the 1x128 activation quantizer of the down
+ * projection's input: q [M, F], s [M, F/128].  F must be a multiple of 128. */
+void oracle_swiglu_quant_1x128(const uint16_t *gu, int64_t M, int64_t F, uint8_t *q, float *s, int mode)
+{
+    int64_t FB = F / 128, b;
+#pragma omp parallel for schedule(static)
+    for (b = 0; b < M * FB; ++b) {
+        int64_t m = b / FB, fb = b % FB, k;
+        uint16_t h[128];
         for (k = 0; k < 128; ++k)
-            qb[k] = (uint8_t)quant_element(bf16_value(xb[k]), sc);
-        s[m * KB + kb] = sc;
+            h[k] = swiglu_element(gu[m * 2 * F + fb * 128 + k], gu[m * 2 * F + F + fb * 128 + k]);
+        quant_act_block(h, q + m * F + fb * 128, s + b, mode);
     }
 }
 

@@ -16,6 +16,12 @@ values are synthetic):
 * output gradients dY (training backward): the activation recipe, from
   their own sub-stream (the article prints no gradient statistics; block
   scaling makes every result invariant to a common power-of-2 factor);
+* gate+up projection outputs (the gated activation's input, [M, 2F], gate
+  columns first): the activation recipe scaled by 2, about the spread of an
+  8B-shaped gate+up GEMM over the inputs above (0.02 * sqrt(4096) = 1.28
+  per unit input, inputs of rms about 1.9 with the outliers); the outliers
+  reach |g| of several hundred, so both tails of the logistic function are
+  exercised;
 * MoE router: fp32 N(0, 1) logits [tokens, experts]; each token goes to its
   top-k experts by logit (softmax is monotone, so this is top-k by
   probability), ties to the lower expert id; rows are grouped by expert, then
@@ -35,6 +41,7 @@ SUB_X = 0
 SUB_W = 1
 SUB_ROUTER = 2
 SUB_DY = 3      # output gradients of the backward (data-gradient) product
+SUB_GU = 4      # gate+up projection outputs (the gated activation's input)
 
 
 def sub_layer(layer: int) -> int:
@@ -65,6 +72,16 @@ def activations(M: int, K: int, seed: int = SEED, sub: int = SUB_X,
     mask = g.random((M, K), dtype=np.float32) < np.float32(outlier_p)
     x[mask] *= np.float32(outlier_mul)
     return f32_to_bf16_bits(x)
+
+
+def gate_up(M: int, F: int, seed: int = SEED, sub: int = SUB_GU, std: float = 2.0) -> np.ndarray:
+    """bf16 payloads [M, 2F]: gate columns 0..F-1, up columns F..2F-1; the
+    activation recipe (N(0,1), Bernoulli(1e-3) entries x 50) times ``std``."""
+    g = _rng(seed, sub)
+    x = g.standard_normal((M, 2 * F), dtype=np.float32)
+    mask = g.random((M, 2 * F), dtype=np.float32) < np.float32(1e-3)
+    x[mask] *= np.float32(50.0)
+    return f32_to_bf16_bits(x * np.float32(std))
 
 
 def weights(N: int, K: int, seed: int = SEED, sub: int = SUB_W, std: float = 0.02) -> np.ndarray:
