@@ -35,6 +35,7 @@ EXPORTS = (
     "quant_act_1x128",
     "quant_act_1x128_t",
     "quant_act_1x128_dual",
+    "swiglu_quant_1x128",
     "quant_w_128x128",
     "quant_w_128x128_batched",
     "quant_w_128x128_dual",
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.quant_act_1x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_act_1x128_t.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_act_1x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
+        L.swiglu_quant_1x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.fp8_block_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
@@ -93,7 +95,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.argtypes = [I32]
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
-        for fn in ("quant_act_1x128", "quant_act_1x128_t", "quant_act_1x128_dual", "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
+        for fn in ("quant_act_1x128", "quant_act_1x128_t", "quant_act_1x128_dual", "swiglu_quant_1x128",
+                   "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
@@ -162,6 +165,22 @@ def quant_act_1x128(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
         xq, xs = out
     _check("quant_act_1x128", lib().quant_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(xs), int(mode), _stream(x)))
     return xq, xs
+
+
+def swiglu_quant_1x128(gu: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 gate+up output [M, 2F] (gate columns first) -> the gated activation,
+    rounded to bf16 and quantized 1x128: (codes uint8 [M, F], scales fp32 [M, F/128])."""
+    gu = _bf16_payload(gu, "gu")
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be 2-D [M, 2F]")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    if out is None:
+        hq = torch.empty((M, F), dtype=torch.uint8, device=gu.device)
+        hs = torch.empty((M, F // 128), dtype=torch.float32, device=gu.device)
+    else:
+        hq, hs = out
+    _check("swiglu_quant_1x128", lib().swiglu_quant_1x128(_ptr(gu), M, F, _ptr(hq), _ptr(hs), int(mode), _stream(gu)))
+    return hq, hs
 
 
 def quant_act_1x128_t(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):

@@ -163,6 +163,22 @@ int quant_act_1x128_dual(const void *x_bf16, int64_t M, int64_t K, void *xq, flo
         fp8bs::launch_quant_act_t(x_bf16, M, K, xqt, xst, scale_mode, (hipStream_t)stream, xq, xs));
 }
 
+int swiglu_quant_1x128(const void *gu_bf16, int64_t M, int64_t F, void *hq, float *hs, int scale_mode, void *stream)
+{
+    if (M < 0 || F <= 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))
+        return FP8BS_INVALID_ARG;
+    if (F % 128 != 0 || F >= kMaxDim || M >= kMaxDim || M * (F / 128) >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (M == 0)
+        return FP8BS_OK;
+    if (!tensor_ok(gu_bf16, 2 * M * F, 16) || !tensor_ok(hq, M * F, 16) || !tensor_ok(hs, M * F, 4))
+        return FP8BS_INVALID_ARG;
+    int st = check_device();
+    if (st != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_swiglu_quant(gu_bf16, M, F, hq, hs, scale_mode, (hipStream_t)stream));
+}
+
 int quant_w_128x128(const void *w_bf16, int64_t N, int64_t K, void *wq, float *ws, int scale_mode, void *stream)
 {
     int st = check_quant(w_bf16, N, K, wq, ws, scale_mode, true);

@@ -36,6 +36,11 @@ hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float
 hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, float *xst, int mode,
                               hipStream_t stream, void *xq = nullptr, float *xs = nullptr);
 
+// The gated activation of gu [M, 2F] (gate columns first), rounded to bf16,
+// then quantized 1x128: hq [M, F], hs [M, F/128] (fp8bs_swiglu.hip).
+hipError_t launch_swiglu_quant(const void *gu, int64_t M, int64_t F, void *hq, float *hs, int mode,
+                               hipStream_t stream);
+
 // One weight tensor of a batched weight quantization (qt, st: the transposed
 // codes [K, N] and scales [K/128, N/128], written by the dual launcher only).
 struct WTensor {

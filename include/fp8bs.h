@@ -127,6 +127,33 @@ FP8BS_API int quant_act_1x128_dual(const void *x_bf16, int64_t M, int64_t K, voi
                                    float *xst, int scale_mode, void *stream);
 
 /*
+ * swiglu_quant_1x128 -- the MLP's gated activation fused with the 1x128
+ * activation quantizer of the down projection's input.  The article keeps
+ * non-linear functions in BF16 and runs the linear layers in FP8 (section
+ * "Technical breakthrough"), and counts quantization kernel overhead in the
+ * gap to the 2x peak (section "Real-world performance gains"); this entry
+ * point takes the gate+up projection's output to the down projection's FP8
+ * input in one pass.
+ *
+ *   gu_bf16 : [M, 2F] bf16 payloads (input): columns 0..F-1 of a row are the
+ *             gate values g, columns F..2F-1 the up values u
+ *   hq      : [M, F] E4M3 codes (output)
+ *   hs      : [M, F/128] fp32 scales (output)
+ *
+ * h[m, f] = the bf16 value nearest (ties to even) to (g * sigma(g)) * u
+ * evaluated in fp64 with sigma(g) = 1 / (1 + exp(-g)), g = gu[m, f],
+ * u = gu[m, F + f]; then (hq, hs) = quant_act_1x128(h, scale_mode), bit for
+ * bit.  (The fp64 evaluation decides only where h lies within about 2^-50 of
+ * a bf16 rounding midpoint.)  Results are unspecified where |g * u| exceeds
+ * the bf16 range or an input is not finite.
+ * Errors: INVALID_ARG (null or misaligned gu_bf16/hq (16 B) or hs (4 B) with
+ * M > 0, M < 0, F <= 0, bad scale_mode), UNSUPPORTED_SHAPE (F % 128 != 0, or
+ * M * F / 128 >= 2^31), UNSUPPORTED_DEVICE.  M == 0 is a no-op.
+ */
+FP8BS_API int swiglu_quant_1x128(const void *gu_bf16, int64_t M, int64_t F, void *hq, float *hs, int scale_mode,
+                                 void *stream);
+
+/*
  * quant_w_128x128 -- weight quantizer, one scale per 128x128 block (article
  * section "Technical breakthrough": 128x128 granularity for weights).  Called
  * on every weight after each optimizer step, it is the per-step scale

@@ -92,6 +92,22 @@ def test_quant_act_validation(fp8bs):
     assert q(NULL, 0, 128, NULL, NULL, 0, NULL) == 0      # M == 0: no-op
 
 
+def test_swiglu_quant_validation(fp8bs):
+    L = fp8bs.lib()
+    q = L.swiglu_quant_1x128
+    assert q(FAKE, 4, 100, FAKE, FAKE, 0, NULL) == 2      # F % 128
+    assert q(FAKE, 1 << 24, 1 << 14, FAKE, FAKE, 0, NULL) == 2   # 2^31 blocks
+    assert q(FAKE, -1, 128, FAKE, FAKE, 0, NULL) == 1     # negative M
+    assert q(FAKE, 4, 0, FAKE, FAKE, 0, NULL) == 1        # F == 0
+    assert q(FAKE, 4, 128, FAKE, FAKE, 2, NULL) == 1      # unknown mode
+    assert q(NULL, 4, 128, FAKE, FAKE, 0, NULL) == 1      # null input
+    assert q(FAKE, 4, 128, NULL, FAKE, 0, NULL) == 1      # null codes
+    assert q(FAKE, 4, 128, FAKE, NULL, 0, NULL) == 1      # null scales
+    assert q(MISAL, 4, 128, FAKE, FAKE, 0, NULL) == 1     # misaligned input
+    assert q(FAKE, 4, 128, MISAL, FAKE, 0, NULL) == 1     # misaligned codes
+    assert q(NULL, 0, 128, NULL, NULL, 0, NULL) == 0      # M == 0: no-op
+
+
 def test_quant_w_validation(fp8bs):
     L = fp8bs.lib()
     q = L.quant_w_128x128
