@@ -63,6 +63,8 @@ DOMINANT = {
     "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, false>", GEMM_SRC,
               "gemm_dma_256x256_dense_m8192_traffic.json"),
     "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
+    # the grouped gate+up call: its row-tile table, the 256-row pass and the short-tile pass
+    "moe": ("fp8_block_grouped_gemm gate+up", GEMM_SRC, "grouped_gemm_moe_gate_up_traffic.json"),
 }
 
 
@@ -489,6 +491,49 @@ def _pmc_means(db, counter):
     return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
 
 
+def _pmc_dispatches(db, counter):
+    """[(dispatch_id, kernel_name, value)] in dispatch order."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    per = {}
+    for kname, val, did in c.execute("select kernel_name, value, dispatch_id from counters_collection "
+                                     "where counter_name = ?", (counter,)):
+        k = per.setdefault(did, [kname, 0.0])
+        k[1] += val
+    return sorted((d, k, v) for d, (k, v) in per.items())
+
+
+def _copy_calibration(db, counter):
+    """Mean counter value of the calibration copies: the runtime's copyBuffer
+    dispatches within a factor of two of the largest one."""
+    vals = [v for _, k, v in _pmc_dispatches(db, counter) if "copybuffer" in k.lower()]
+    if not vals:
+        raise SystemExit("no calibration copy in the counter database")
+    big = [v for v in vals if v >= 0.5 * max(vals)]
+    return sum(big) / len(big)
+
+
+def _grouped_gate_up_calls(db, counter):
+    """Mean value per grouped gate+up call of the MoE step, and the number of
+    calls: the table and GEMM dispatches that follow an activation quantizer
+    (the down call follows the gated activation instead)."""
+    calls, cur, after_quant = [], None, False
+    for _, k, v in _pmc_dispatches(db, counter):
+        if "grouped_tile_table_kernel" in k:
+            cur = [v] if after_quant else None
+            if cur is not None:
+                calls.append(cur)
+            after_quant = False
+        elif "gemm_dma_kernel" in k and cur is not None:
+            cur.append(v)
+        else:
+            cur = None
+            after_quant = "quant_act_kernel" in k
+    if not calls:
+        raise SystemExit("no grouped gate+up call found in the counter database")
+    return sum(sum(c) for c in calls) / len(calls), len(calls)
+
+
 def summarize_pmc(fetch_db, write_db, workload, command, out=None):
     """Write the traffic record of `workload`'s dominant kernel (to profiles/
     unless `out` names another file) and return it."""
@@ -501,14 +546,17 @@ def summarize_pmc(fetch_db, write_db, workload, command, out=None):
         if not hits:
             raise SystemExit("no kernel matched in the counter database")
         return hits[0][1]
-    # torch's device-to-device copy of one buffer is the runtime's blit kernel
-    is_copy = lambda k: "copybuffer" in k.lower()  # noqa: E731
     is_dom = lambda k: k.startswith("void " + kprefix) or k.startswith(kprefix)  # noqa: E731
-    # the calibration copy moves COPY_BYTES in and COPY_BYTES out per launch
-    copy_f, _ = pick(fetch, is_copy)
-    copy_w, _ = pick(write, is_copy)
-    kf, nf = pick(fetch, is_dom)
-    kw, nw = pick(write, is_dom)
+    # the calibration copy moves COPY_BYTES in and COPY_BYTES out per launch; smaller copies of the
+    # workload itself (an upload of routing offsets) are left out
+    copy_f = _copy_calibration(fetch_db, "FETCH_SIZE")
+    copy_w = _copy_calibration(write_db, "WRITE_SIZE")
+    if workload == "moe":
+        kf, nf = _grouped_gate_up_calls(fetch_db, "FETCH_SIZE")
+        kw, nw = _grouped_gate_up_calls(write_db, "WRITE_SIZE")
+    else:
+        kf, nf = pick(fetch, is_dom)
+        kw, nw = pick(write, is_dom)
     f_scale = COPY_BYTES / (copy_f * 1024.0)
     w_scale = COPY_BYTES / (copy_w * 1024.0)
     rec = {"kernel": kprefix, "workload": workload, "command": command,
@@ -657,6 +705,7 @@ def main():
         t = timer.avg_ms("grouped_gate_up")
         m, n, k = shapes["gate_up"]
         ach = 2.0 * m * n * k / (t * 1e-3) / 1e12
+        traffic, tsrc = traffic_for("moe")
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens top-8 "
@@ -664,7 +713,7 @@ def main():
                                       "the down projection, grouped down K768 N2048"},
                "roofline": {"kernel": "fp8_block_grouped_gemm gate+up", "bound": "mfma", "achieved": round(ach, 1),
                             "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
-                            "traffic": None},
+                            "traffic": traffic, "traffic_source": tsrc},
                "kernels": kernels}
         cpu = None
 

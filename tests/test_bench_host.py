@@ -61,6 +61,36 @@ def test_traffic_record_scales_by_the_copy_calibration(bench, tmp_path):
     assert json.load(open(tmp_path / "rec.json")) == rec
 
 
+def test_moe_record_sums_each_gate_up_call(bench, tmp_path):
+    """The MoE record takes the grouped gate+up call (table + 256-row pass +
+    short-tile pass after the activation quantizer), not the down call that
+    follows the gated activation."""
+    copy = "__amd_rocclr_copyBuffer"
+    gib_kib = bench.COPY_BYTES / 1024
+    seq = ["void fp8bs::quant_w_kernel<0>(fp8bs::QWArgs)", "void fp8bs::quant_act_kernel<0>(...)",
+           "void fp8bs::grouped_tile_table_kernel<256, 128>(...)",
+           "void fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, true, false, false, false>(fp8bs::GemmArgs)",
+           "void fp8bs::gemm_dma_kernel<128, 256, 2, 4, false, true, false, false, false>(fp8bs::GemmArgs)",
+           "void fp8bs::swiglu_quant_kernel<0>(...)",
+           "void fp8bs::grouped_tile_table_kernel<256, 128>(...)",
+           "void fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, true, false, false, false>(fp8bs::GemmArgs)",
+           "void fp8bs::gemm_dma_kernel<128, 256, 2, 4, false, true, false, false, false>(fp8bs::GemmArgs)"]
+    vals = [1000.0, 100.0, 1.0, 500.0, 50.0, 70.0, 2.0, 300.0, 30.0]
+    rows, d = [], 0
+    for step in range(2):  # two steps; the second gate+up call moves 2x as much
+        for k, v in zip(seq, vals):
+            d += 1
+            rows.append((k, v * (1 + step), d))
+    _counter_db(tmp_path / "f.db", "FETCH_SIZE", rows + [(copy, gib_kib / 2, d + 1)])
+    _counter_db(tmp_path / "w.db", "WRITE_SIZE", rows + [(copy, gib_kib, d + 1)])
+    rec = bench.summarize_pmc(str(tmp_path / "f.db"), str(tmp_path / "w.db"), "moe", "test command",
+                              out=str(tmp_path / "rec.json"))
+    assert rec["launches"] == [2, 2]
+    per_call = (1.0 + 500.0 + 50.0) * 1.5  # mean over the two steps
+    assert rec["hbm_fetch_bytes_per_launch"] == pytest.approx(per_call * 1024 * 2.0)
+    assert rec["hbm_write_bytes_per_launch"] == pytest.approx(per_call * 1024)
+
+
 def test_no_kernel_in_the_database_is_an_error(bench, tmp_path):
     _counter_db(tmp_path / "f.db", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 1.0, 1)])
     _counter_db(tmp_path / "w.db", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1.0, 1)])
