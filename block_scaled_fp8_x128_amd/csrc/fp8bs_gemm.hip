@@ -1428,12 +1428,14 @@ static hipError_t run_skinny_t(GemmArgs a, bool out_f32, hipStream_t stream)
 // The weight-streaming kernel on bf16 activations (M <= 16: one 16-row X
 // tile), quantizing them itself with EXACT (QX = 1) or POW2 (QX = 2) scales,
 // with the 64- or 32-row W tiles the plain kernel would pick (linear_fused
-// admits no other shape).
+// admits no other shape).  With 64-row tiles one K block in flight per wave
+// measured best (92 VGPRs, four workgroups per CU): more depth costs
+// occupancy, and the other workgroups' loads hide the latency better.
 template <int QX>
 static hipError_t run_skinny_qx(GemmArgs a, bool out_f32, hipStream_t stream)
 {
     if (a.N % 64 == 0 && a.N / 64 >= 256)
-        return run_skinny_t<1, 4, 4, QX>(a, out_f32, stream);
+        return run_skinny_t<1, 4, 1, QX>(a, out_f32, stream);
     return run_skinny_t<1, 2, 4, QX>(a, out_f32, stream);
 }
 
@@ -1448,8 +1450,8 @@ static hipError_t run_skinny(GemmArgs a, bool out_f32, hipStream_t stream)
     const int tn = (N % 64 == 0 && N / 64 >= 256) ? 4 : (N % 32 == 0 && N / 32 >= 256) ? 2 : 1;
     const int tm = M <= 16 ? 1 : M <= 32 ? 2 : 4;
     if (tm == 1) {
-        if (tn == 4)
-            return run_skinny_t<1, 4, 4>(a, out_f32, stream);
+        if (tn == 4) // two K blocks in flight per wave (80 VGPRs) stream faster than four (196)
+            return run_skinny_t<1, 4, 2>(a, out_f32, stream);
         if (tn == 2)
             return run_skinny_t<1, 2, 4>(a, out_f32, stream);
         return run_skinny_t<1, 1, 6>(a, out_f32, stream);
