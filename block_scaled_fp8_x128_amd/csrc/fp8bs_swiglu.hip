@@ -27,10 +27,12 @@
 // value) and rounded to bf16 from there by the hardware conversion.  That
 // rounding agrees with the rounding of the fp64 value unless the fp32 value
 // lies within a few fp32 units of a bf16 rounding midpoint; such elements
-// (low 16 bits of the fp32 pattern within 64 of 0x8000), and every element
-// whose operands or result leave the range where the fp32 error bound holds
-// (g < -64, h zero, subnormal, infinite or NaN), are recomputed in fp64 and
-// rounded from there.  About 0.2% of elements take the fp64 path.
+// (low 16 bits of the fp32 pattern within 16 of 0x8000: over three times the
+// bound), and every element whose operands or result leave the range where
+// the fp32 error bound holds (g < -64, h zero, subnormal, infinite or NaN),
+// are recomputed in fp64 and rounded from there.  About 0.05% of elements
+// take the fp64 path; the window is kept narrow because a wave runs the fp64
+// path for an element slot whenever one of its lanes needs it.
 #include "fp8bs_device.hpp"
 #include "fp8bs_internal.hpp"
 
@@ -86,7 +88,7 @@ __device__ __forceinline__ float one_plus_exp_neg(float g)
 // When h is a normal fp32, so is g * u (|g * u| >= |h|), and g * u is then
 // exact (two 8-bit significands); the relative error of h is that of
 // sigma(g) plus one rounding, below about 5 units in the last place (the
-// exponential about 2, the reciprocal 1).  Elements within 64 units of a bf16
+// exponential about 2, the reciprocal 1).  Elements within 16 units of a bf16
 // rounding midpoint, or outside the range where that bound holds (g < -64, h
 // zero, subnormal, infinite or NaN), are flagged for fp64.  The tests are
 // combined without short-circuit branches so that the fp32 path stays
@@ -97,7 +99,7 @@ __device__ __forceinline__ float swiglu_fast(float g, float u, bool &ok)
     const float h = (g * u) * sig;
     const uint32_t b = __float_as_uint(h);
     constexpr int NORMAL = 0x008 | 0x100; // negative normal | positive normal
-    ok = (g >= -64.0f) & __builtin_amdgcn_classf(h, NORMAL) & (((b & 0xFFFFu) - (0x8000u - 64u)) > 128u);
+    ok = (g >= -64.0f) & __builtin_amdgcn_classf(h, NORMAL) & (((b & 0xFFFFu) - (0x8000u - 16u)) > 32u);
     return h;
 }
 
