@@ -108,6 +108,40 @@ def test_swiglu_quant_special_values(fp8bs, orc, mode):
     _check(fp8bs, orc, gu, mode, "special")
 
 
+def _midpoint_distance_units(h):
+    """Distance of float64 values to the nearest bf16 rounding midpoint, in units
+    of the fp32 spacing at each value (normal fp32 range only)."""
+    h = np.abs(h)
+    e = np.floor(np.log2(h))
+    unit = np.exp2(e - 23)                  # fp32 spacing in [2^e, 2^(e+1))
+    half = np.exp2(e - 8)                   # half the bf16 spacing there
+    r = np.mod(h, 2 * half)                 # position within a bf16 interval
+    return np.abs(r - half) / unit
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_swiglu_quant_near_the_fp64_window(fp8bs, orc, mode):
+    """Elements whose value lies 16 to 64 fp32 units from a bf16 midpoint: the
+    fp32 path alone decides their rounding (the fp64 recompute covers 16 and
+    less), so these check its error bound where it matters."""
+    say("swiglu_quant_1x128 near the fp64 window, mode=%d" % mode)
+    rng = np.random.default_rng(23)
+    n = 1 << 22
+    g = synth.f32_to_bf16_bits((rng.standard_normal(n) * 4).astype(np.float32))
+    u = synth.f32_to_bf16_bits((rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32))
+    gf = synth.bf16_bits_to_f32(g).astype(np.float64)
+    uf = synth.bf16_bits_to_f32(u).astype(np.float64)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        h = (gf / (1.0 + np.exp(-gf))) * uf
+        d = _midpoint_distance_units(h)
+    pick = (gf >= -64) & (np.abs(h) >= 2.0 ** -100) & (np.abs(h) < 2.0 ** 100) & (d > 16) & (d <= 64)
+    F = 1280
+    k = (int(pick.sum()) // F) * F
+    assert k >= 2 * F, int(pick.sum())
+    gp, up = g[pick][:k].reshape(-1, F), u[pick][:k].reshape(-1, F)
+    _check(fp8bs, orc, np.concatenate([gp, up], axis=1), mode, "near the window (%d elements)" % k)
+
+
 def test_swiglu_quant_empty_and_errors(fp8bs):
     say("swiglu_quant_1x128 empty and errors")
     lib = fp8bs.lib()
