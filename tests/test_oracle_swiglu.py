@@ -164,6 +164,32 @@ def test_swiglu_matches_decimal_evaluation(orc):
     assert near < gp.size // 20
 
 
+@pytest.mark.parametrize("up", [0x3F80, 0xC040])  # u = 1 and u = -3
+def test_swiglu_every_gate_value(orc, up):
+    """Every finite bf16 gate value against the 60-digit evaluation rounded
+    exactly (values within 2^-48 of a midpoint may take either neighbour).
+    For g < -200 the exact |h| is below 2^-134 and rounds to a zero carrying
+    the sign of g * u; signed zeros of g keep theirs."""
+    p = np.arange(1 << 16, dtype=np.uint32)
+    gp = p[(p & 0x7F80) != 0x7F80].astype(np.uint16)
+    h = orc.swiglu_bf16(np.stack([gp, np.full_like(gp, up)], axis=1))[:, 0]
+    u_neg = bool(up & 0x8000)
+    gf = synth.bf16_bits_to_f32(gp)
+    for i in range(gp.size):
+        g_neg = bool(gp[i] & 0x8000)
+        if gf[i] == 0 or gf[i] < -200:
+            want = 0x8000 if g_neg != u_neg else 0x0000
+            assert int(h[i]) == want, (hex(gp[i]), hex(h[i]))
+            continue
+        ex = _swiglu_decimal(int(gp[i]), up)
+        if _near_midpoint(ex):
+            lo = _rne_bf16_exact(ex * (1 - Fraction(1, 1 << 40)))
+            hi = _rne_bf16_exact(ex * (1 + Fraction(1, 1 << 40)))
+            assert int(h[i]) in (lo, hi), hex(gp[i])
+        else:
+            assert int(h[i]) == _rne_bf16_exact(ex), (hex(gp[i]), hex(h[i]), hex(_rne_bf16_exact(ex)))
+
+
 def test_swiglu_fp64_reading_where_sigma_rounds_to_one(orc):
     """For g >= 40, 1 + exp(-g) == 1 in fp64, so the reading gives
     h = RN_bf16(g * u) exactly, ties (exact bf16 midpoints g * u) to even."""
