@@ -177,6 +177,18 @@ def quant_w_128x128(w_bf16, mode: int = SCALE_EXACT):
     return q, s
 
 
+def quant_act_1x128_gather(x_bf16, rows, mode: int = SCALE_EXACT):
+    """quant_act_1x128 of the gathered rows x[rows] (MoE dispatch: token rows in
+    expert order, a token repeated once per expert it is routed to).
+    x_bf16: uint16 [T, K]; rows: int [M] in [0, T) -> (codes [M, K], scales [M, K/128]).
+    The gather is numpy's; every arithmetic step is the quantizer's."""
+    x = _c(x_bf16, np.uint16)
+    r = np.asarray(rows, dtype=np.int64)
+    if r.size and (r.min() < 0 or r.max() >= x.shape[0]):
+        raise ValueError("row index out of range")
+    return quant_act_1x128(x[r].reshape(r.size, x.shape[1]), mode)
+
+
 def quant_act_1x128_t(x_bf16, mode: int = SCALE_EXACT):
     """quant_act_1x128 of X^T: 1x128 blocks down the columns of X [M, K], written as
     codes [K, M] and scales [K, M/128] (the weight gradient's operands)."""

@@ -274,3 +274,20 @@ def test_subnormal_scale_blocks(orc):
     assert (q[:, 0] == 0x7E).all()
     qp, sp = orc.quant_act_1x128(blocks, orc.SCALE_POW2)
     assert ((qp[:, 0] >= 0x76) & (qp[:, 0] <= 0x7E)).all()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_quant_act_gather_equals_quantize_then_gather(orc, mode):
+    """The 1x128 blocks lie along rows, so quantizing the gathered rows equals
+    gathering the rows' codes and scales (the MoE dispatch reading), with
+    repeated, skipped and reordered rows."""
+    x = synth.activations(64, 384, sub=77)
+    g = np.random.default_rng(5)
+    rows = np.concatenate([g.integers(0, 64, 300), [0, 63, 63, 0]]).astype(np.int32)
+    q, s = orc.quant_act_1x128_gather(x, rows, mode)
+    q0, s0 = orc.quant_act_1x128(x, mode)
+    assert np.array_equal(q, q0[rows]) and np.array_equal(s.view(np.uint32), s0[rows].view(np.uint32))
+    q1, s1 = orc.quant_act_1x128_gather(x, np.zeros(0, dtype=np.int32), mode)
+    assert q1.shape == (0, 384) and s1.shape == (0, 3)
+    with pytest.raises(ValueError):
+        orc.quant_act_1x128_gather(x, np.array([64], dtype=np.int32), mode)
