@@ -427,18 +427,23 @@ def decode_workload(fp8bs, dev, mode):
     return step, separate, pairs, flops
 
 
+T_TOKENS = 8192  # tokens of the MoE layer (each routed to 8 of 128 experts)
+
+
 def moe_workload(fp8bs, dev, mode):
     # POW2 scales go to the entry points that apply them through the matrix cores
     gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
     grouped = fp8bs.fp8_block_grouped_gemm_pow2 if mode else fp8bs.fp8_block_grouped_gemm
     import synth
     import torch
-    E, H, F, T, TOPK = 128, 2048, 768, 8192, 8
+    E, H, F, T, TOPK = 128, 2048, 768, T_TOKENS, 8
     row_token, offs = synth.moe_routing(T, E, TOPK)
     Mt = int(offs[-1])
     log("MoE: %d routed rows, per-expert rows min %d max %d" % (Mt, int(np.diff(offs).min()), int(np.diff(offs).max())))
     x_tok = synth.activations(T, H, sub=synth.SUB_X)
-    x1 = bf16_dev(x_tok[row_token], dev)
+    # the dispatch: each routed row reads its token's row (quantized on the way, in expert order)
+    xt = bf16_dev(x_tok, dev)
+    rows_d = torch.from_numpy(np.ascontiguousarray(row_token, dtype=np.int32)).to(dev)
     w1 = bf16_dev(synth.expert_weights(E, 2 * F, H, sub=synth.SUB_W).reshape(E * 2 * F, H), dev)
     w2 = bf16_dev(synth.expert_weights(E, H, F, sub=synth.SUB_W + 1).reshape(E * H, F), dev)
     offs_d = torch.from_numpy(offs).to(dev)
@@ -460,7 +465,8 @@ def moe_workload(fp8bs, dev, mode):
         maybe(timer, "quant_w_experts", lambda: fp8bs.quant_w_128x128_batched([w1, w2], mode,
                                                                                outs=[(b["w1q"], b["w1s"]),
                                                                                      (b["w2q"], b["w2s"])]))
-        maybe(timer, "quant_act_gate_up", lambda: fp8bs.quant_act_1x128(x1, mode, out=(b["x1q"], b["x1s"])))
+        maybe(timer, "quant_act_gather_gate_up", lambda: fp8bs.quant_act_1x128_gather(xt, rows_d, mode,
+                                                                                    out=(b["x1q"], b["x1s"])))
         maybe(timer, "grouped_gate_up", lambda: grouped(
             b["x1q"], b["x1s"], b["w1q"].view(E, 2 * F, H), b["w1s"].view(E, 2 * F // 128, H // 128), offs_d,
             out=b["y1"], workspace=b["wk1"]))
@@ -515,7 +521,7 @@ def _copy_calibration(db, counter):
 
 def _grouped_gate_up_calls(db, counter):
     """Mean value per grouped gate+up call of the MoE step, and the number of
-    calls: the table and GEMM dispatches that follow an activation quantizer
+    calls: the table and GEMM dispatches that follow the dispatch quantizer
     (the down call follows the gated activation instead)."""
     calls, cur, after_quant = [], None, False
     for _, k, v in _pmc_dispatches(db, counter):
@@ -528,7 +534,7 @@ def _grouped_gate_up_calls(db, counter):
             cur.append(v)
         else:
             cur = None
-            after_quant = "quant_act_kernel" in k
+            after_quant = "quant_act_kernel" in k or "quant_act_gather_kernel" in k
     if not calls:
         raise SystemExit("no grouped gate+up call found in the counter database")
     return sum(sum(c) for c in calls) / len(calls), len(calls)
@@ -698,7 +704,9 @@ def main():
             nbytes = m * k + m * k // 128 * 4 + E * n * k * (1 + 4 / 16384) + m * n * 2
             kernels["grouped_" + name] = {**mfma_entry(t, 2.0 * m * n * k), **hbm_entry(t, nbytes)}
         m, _, k = shapes["gate_up"]
-        kernels["quant_act_gate_up"] = hbm_entry(timer.avg_ms("quant_act_gate_up"), m * k * 3 + m * k // 128 * 4)
+        # dispatch quantizer: the token rows read once (T x K bf16), the row indices, codes and scales written
+        kernels["quant_act_gather_gate_up"] = hbm_entry(timer.avg_ms("quant_act_gather_gate_up"),
+                                                        T_TOKENS * k * 2 + m * 4 + m * k + m * k // 128 * 4)
         # gated activation + quantizer: 2 bf16 in, 1 code out per element of h, one fp32 per 128
         m, _, k = shapes["down"]
         kernels["swiglu_quant_down"] = hbm_entry(timer.avg_ms("swiglu_quant_down"), m * k * 5 + m * k // 128 * 4)
@@ -720,8 +728,9 @@ def main():
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens top-8 "
-                                      "(65536 rows); grouped gate+up K2048 N1536, the gated activation quantized for "
-                                      "the down projection, grouped down K768 N2048"},
+                                      "(65536 rows); the dispatch quantizing token rows into expert order, grouped "
+                                      "gate+up K2048 N1536, the gated activation quantized for the down projection, "
+                                      "grouped down K768 N2048"},
                "roofline": {"kernel": "fp8_block_grouped_gemm gate+up", **roof,
                             "algorithmic_bytes_per_launch": gbytes, "algorithmic_flop_per_launch": gflop,
                             "traffic": traffic, "traffic_source": tsrc},

@@ -35,6 +35,7 @@ EXPORTS = (
     "quant_act_1x128",
     "quant_act_1x128_t",
     "quant_act_1x128_dual",
+    "quant_act_1x128_gather",
     "swiglu_quant_1x128",
     "quant_w_128x128",
     "quant_w_128x128_batched",
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.quant_act_1x128_t.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_act_1x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
         L.swiglu_quant_1x128.argtypes = [P, I64, I64, P, P, I32, P]
+        L.quant_act_1x128_gather.argtypes = [P, I64, I64, P, I64, P, P, I32, P]
         L.fp8_block_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
         for fn in ("quant_act_1x128", "quant_act_1x128_t", "quant_act_1x128_dual", "swiglu_quant_1x128",
+                   "quant_act_1x128_gather",
                    "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
@@ -164,6 +167,26 @@ def quant_act_1x128(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     else:
         xq, xs = out
     _check("quant_act_1x128", lib().quant_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(xs), int(mode), _stream(x)))
+    return xq, xs
+
+
+def quant_act_1x128_gather(x: torch.Tensor, rows: torch.Tensor, mode: int = SCALE_EXACT, out=None):
+    """bf16 token rows [T, K] and int32 row indices [M] (device) -> quant_act_1x128 of
+    x[rows]: (codes uint8 [M, K], scales fp32 [M, K/128])."""
+    x = _bf16_payload(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [T, K]")
+    if rows.dtype != torch.int32 or rows.dim() != 1 or not rows.is_contiguous() or rows.device != x.device:
+        raise ValueError("rows must be a contiguous 1-D int32 tensor on x's device")
+    T, K = x.shape
+    M = rows.shape[0]
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        xs = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    else:
+        xq, xs = out
+    _check("quant_act_1x128_gather", lib().quant_act_1x128_gather(_ptr(x), T, K, _ptr(rows), M, _ptr(xq), _ptr(xs),
+                                                                 int(mode), _stream(x)))
     return xq, xs
 
 

@@ -163,6 +163,25 @@ int quant_act_1x128_dual(const void *x_bf16, int64_t M, int64_t K, void *xq, flo
         fp8bs::launch_quant_act_t(x_bf16, M, K, xqt, xst, scale_mode, (hipStream_t)stream, xq, xs));
 }
 
+int quant_act_1x128_gather(const void *x_bf16, int64_t T, int64_t K, const int32_t *rows, int64_t M, void *xq,
+                           float *xs, int scale_mode, void *stream)
+{
+    if (T < 0 || M < 0 || K <= 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))
+        return FP8BS_INVALID_ARG;
+    if (K % 128 != 0 || K >= kMaxDim || T >= kMaxDim || M >= kMaxDim || M * (K / 128) >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (M == 0)
+        return FP8BS_OK;
+    if (!tensor_ok(x_bf16, T * K, 16) || !tensor_ok(rows, M, 4) || !tensor_ok(xq, M * K, 16) ||
+        !tensor_ok(xs, M * K, 4))
+        return FP8BS_INVALID_ARG;
+    int st = check_device();
+    if (st != FP8BS_OK)
+        return st;
+    return status_of(
+        fp8bs::launch_quant_act_gather(x_bf16, T, K, rows, M, xq, xs, scale_mode, (hipStream_t)stream));
+}
+
 int swiglu_quant_1x128(const void *gu_bf16, int64_t M, int64_t F, void *hq, float *hs, int scale_mode, void *stream)
 {
     if (M < 0 || F <= 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))

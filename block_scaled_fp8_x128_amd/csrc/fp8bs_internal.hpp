@@ -36,6 +36,10 @@ hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float
 hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, float *xst, int mode,
                               hipStream_t stream, void *xq = nullptr, float *xs = nullptr);
 
+// quant_act_1x128 of x[rows[m]] for m < M (x [T, K]; an index outside
+// [0, T) reads as a zero row) (fp8bs_route.hip).
+hipError_t launch_quant_act_gather(const void *x, int64_t T, int64_t K, const int32_t *rows, int64_t M, void *xq,
+                                   float *xs, int mode, hipStream_t stream);
 // The gated activation of gu [M, 2F] (gate columns first), rounded to bf16,
 // then quantized 1x128: hq [M, F], hs [M, F/128] (fp8bs_swiglu.hip).
 hipError_t launch_swiglu_quant(const void *gu, int64_t M, int64_t F, void *hq, float *hs, int mode,

@@ -127,6 +127,29 @@ FP8BS_API int quant_act_1x128_dual(const void *x_bf16, int64_t M, int64_t K, voi
                                    float *xst, int scale_mode, void *stream);
 
 /*
+ * quant_act_1x128_gather -- the activation quantizer over gathered rows: the
+ * MoE dispatch.  The article runs its recipe on a mixture-of-experts model
+ * (section "Real-world performance gains"); an MoE layer's grouped GEMM takes
+ * each token's row once per expert it is routed to, in expert order.  The
+ * 1x128 blocks lie along a row, so this equals quant_act_1x128 of the
+ * gathered matrix, computed without materializing it.
+ *
+ *   x_bf16 : [T, K] bf16 payloads (input): the token rows
+ *   rows   : [M] int32 row indices into x (device memory, never read by the
+ *            host)
+ *   xq     : [M, K] E4M3 codes (output); xs : [M, K/128] fp32 scales (output)
+ *
+ * xq[m], xs[m] = quant_act_1x128(x[rows[m]]), bit for bit.  An index outside
+ * [0, T) yields an all-zero row (codes 0, scales 1); no memory outside x is
+ * read.  Errors: INVALID_ARG (T < 0, M < 0, K <= 0, bad scale_mode, null or
+ * misaligned x (16 B, when T > 0), rows (4 B), xq (16 B), xs (4 B) with
+ * M > 0), UNSUPPORTED_SHAPE (K % 128 != 0, M * K / 128 >= 2^31),
+ * UNSUPPORTED_DEVICE.  M == 0 is a no-op.
+ */
+FP8BS_API int quant_act_1x128_gather(const void *x_bf16, int64_t T, int64_t K, const int32_t *rows, int64_t M,
+                                     void *xq, float *xs, int scale_mode, void *stream);
+
+/*
  * swiglu_quant_1x128 -- the MLP's gated activation fused with the 1x128
  * activation quantizer of the down projection's input.  The article keeps
  * non-linear functions in BF16 and runs the linear layers in FP8 (section

@@ -92,6 +92,23 @@ def test_quant_act_validation(fp8bs):
     assert q(NULL, 0, 128, NULL, NULL, 0, NULL) == 0      # M == 0: no-op
 
 
+def test_quant_act_gather_validation(fp8bs):
+    L = fp8bs.lib()
+    q = L.quant_act_1x128_gather
+    assert q(FAKE, 8, 100, FAKE, 4, FAKE, FAKE, 0, NULL) == 2       # K % 128
+    assert q(FAKE, 8, 1 << 14, FAKE, 1 << 24, FAKE, FAKE, 0, NULL) == 2   # 2^31 blocks
+    assert q(FAKE, -1, 128, FAKE, 4, FAKE, FAKE, 0, NULL) == 1      # negative T
+    assert q(FAKE, 8, 128, FAKE, -1, FAKE, FAKE, 0, NULL) == 1      # negative M
+    assert q(FAKE, 8, 0, FAKE, 4, FAKE, FAKE, 0, NULL) == 1         # K == 0
+    assert q(FAKE, 8, 128, FAKE, 4, FAKE, FAKE, 2, NULL) == 1       # unknown mode
+    assert q(NULL, 8, 128, FAKE, 4, FAKE, FAKE, 0, NULL) == 1       # null input
+    assert q(FAKE, 8, 128, NULL, 4, FAKE, FAKE, 0, NULL) == 1       # null rows
+    assert q(FAKE, 8, 128, FAKE, 4, NULL, FAKE, 0, NULL) == 1       # null codes
+    assert q(FAKE, 8, 128, FAKE, 4, FAKE, NULL, 0, NULL) == 1       # null scales
+    assert q(MISAL, 8, 128, FAKE, 4, FAKE, FAKE, 0, NULL) == 1      # misaligned input
+    assert q(NULL, 0, 128, NULL, 0, NULL, NULL, 0, NULL) == 0       # M == 0: no-op
+
+
 def test_swiglu_quant_validation(fp8bs):
     L = fp8bs.lib()
     q = L.swiglu_quant_1x128
