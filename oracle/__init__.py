@@ -67,6 +67,12 @@ def lib():
         L.oracle_gemm_1x128_sampled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.oracle_grouped_gemm_sampled.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P, I64, P]
+        L.oracle_e4m3_x512_table.argtypes = [P]
+        for f in (L.oracle_gemm_full, L.oracle_gemm_1x128_full):
+            f.restype = ctypes.c_int
+            f.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_grouped_gemm_full.restype = ctypes.c_int
+        L.oracle_grouped_gemm_full.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -276,4 +282,52 @@ def grouped_gemm_sampled(xq, xs, wq, ws, offsets, rows, cols) -> np.ndarray:
     y = np.empty(rows.shape, dtype=np.float64)
     lib().oracle_grouped_gemm_sampled(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offs), E, M, N, K,
                                       _ptr(rows), _ptr(cols), rows.size, _ptr(y))
+    return y
+
+
+# ---- the same GEMMs, every output, at full configuration sizes -----------------
+# Codes decoded once through a table of decode(c) * 2^9; each 128-wide block's
+# dot product summed in fp64, which is exact (all partial sums are integers
+# below 2^43), so the outputs are bit-identical to gemm / gemm_1x128 /
+# grouped_gemm above.
+
+def e4m3_x512_table() -> np.ndarray:
+    """The full-output GEMMs' table: decode(c) * 2^9 for c = 0 .. 255 (NaN codes NaN)."""
+    t = np.empty(256, dtype=np.float64)
+    lib().oracle_e4m3_x512_table(_ptr(t))
+    return t
+
+
+def _full(fn, xq, xs, wq, ws, ncols_of_w):
+    xq, wq = _c(xq, np.uint8), _c(wq, np.uint8)
+    xs, ws = _c(xs, np.float32), _c(ws, np.float32)
+    M, K = xq.shape
+    N = ncols_of_w(wq)
+    y = np.empty((M, N), dtype=np.float64)
+    if fn(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y)) != 0:
+        raise MemoryError("oracle: no memory for the decoded operands")
+    return y
+
+
+def gemm_full(xq, xs, wq, ws) -> np.ndarray:
+    """gemm(), every output, bit-identical, fast enough for the 8B-shaped layers."""
+    return _full(lib().oracle_gemm_full, xq, xs, wq, ws, lambda w: w.shape[0])
+
+
+def gemm_1x128_full(xq, xs, wq, ws) -> np.ndarray:
+    """gemm_1x128(), every output, bit-identical."""
+    return _full(lib().oracle_gemm_1x128_full, xq, xs, wq, ws, lambda w: w.shape[0])
+
+
+def grouped_gemm_full(xq, xs, wq, ws, offsets) -> np.ndarray:
+    """grouped_gemm(), every output, bit-identical."""
+    xq, wq = _c(xq, np.uint8), _c(wq, np.uint8)
+    xs, ws = _c(xs, np.float32), _c(ws, np.float32)
+    offs = _c(np.asarray(offsets, dtype=np.int32), np.int32)
+    M, K = xq.shape
+    E, N, _ = wq.shape
+    y = np.empty((M, N), dtype=np.float64)
+    if lib().oracle_grouped_gemm_full(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offs), E, M, N, K,
+                                      _ptr(y)) != 0:
+        raise MemoryError("oracle: no memory for the decoded operands")
     return y

@@ -50,6 +50,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -428,6 +429,155 @@ void oracle_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, 
         int64_t r = i / N, e = expert_of_row(offs, E, r);
         y[i] = (e < 0) ? NAN : gemm_element(xq, xs, wq + e * wstride, ws + e * sstride, K, r, i % N);
     }
+}
+
+/* ---- the same GEMMs, every output, at full configuration sizes ------------
+ *
+ * gemm_element re-decodes both codes of every product.  The functions below
+ * compute exactly the same numbers with the codes decoded once:
+ *   - a 256-entry table holds decode(c) * 2^9 for every code c, filled from
+ *     oracle_e4m3_decode (NaN for the two NaN codes);
+ *   - X and W are turned into fp64 arrays of those integers;
+ *   - each 128-wide block's dot product is summed in fp64.  Every product is an
+ *     integer below 2^36 in magnitude (229376^2 < 2^36) and every partial sum
+ *     of at most 128 of them an integer below 2^43 < 2^53, so each addition is
+ *     exact whatever the order: the block sum equals gemm_element's int64 P.
+ *     (That is why the compiler may vectorize the reduction.)
+ *   - the scale product, the 2^-18 and the sum over blocks in ascending kb are
+ *     the same fp64 operations as in gemm_element, so every output is
+ *     bit-identical to oracle_gemm's.  A NaN code makes its outputs NaN.
+ * Outputs are computed in tiles of TR rows x TC columns so that a tile's
+ * operands stay in cache; the arithmetic per output is unchanged. */
+
+static double e4m3_x512_table[256];
+
+static void build_e4m3_x512_table(void)
+{
+    int c;
+    for (c = 0; c < 256; ++c)
+        e4m3_x512_table[c] = ldexp(oracle_e4m3_decode((uint32_t)c), 9);
+}
+
+/* the table, for the tests that pin it against oracle_e4m3_decode */
+void oracle_e4m3_x512_table(double *out)
+{
+    int c;
+    build_e4m3_x512_table();
+    for (c = 0; c < 256; ++c)
+        out[c] = e4m3_x512_table[c];
+}
+
+static void decode_x512(const uint8_t *q, int64_t n, double *d)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        d[i] = e4m3_x512_table[q[i]];
+}
+
+static double block_dot(const double *a, const double *b)
+{
+    double p = 0.0;
+    int k;
+#pragma omp simd reduction(+ : p)
+    for (k = 0; k < 128; ++k)
+        p += a[k] * b[k];
+    return p;
+}
+
+enum { TR = 8, TC = 32 };
+
+/* Rows r0 .. r1-1 of Y = X W^T from decoded operands; ws_of_col selects the
+ * weight-scale layout: 0 = [N/128, K/128] blocks, 1 = [N, K/128] rows. */
+static void gemm_rows_decoded(const double *xd, const float *xs, const double *wd, const float *ws, int64_t r0,
+                              int64_t r1, int64_t N, int64_t K, int ws_of_col, double *y)
+{
+    int64_t KB = K / 128, tiles_r = (r1 - r0 + TR - 1) / TR, tiles_c = (N + TC - 1) / TC, t;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < tiles_r * tiles_c; ++t) {
+        int64_t m0 = r0 + (t / tiles_c) * TR, n0 = (t % tiles_c) * TC, m, n, kb;
+        int64_t m1 = m0 + TR < r1 ? m0 + TR : r1, n1 = n0 + TC < N ? n0 + TC : N;
+        for (m = m0; m < m1; ++m)
+            for (n = n0; n < n1; ++n)
+                y[m * N + n] = 0.0;
+        for (kb = 0; kb < KB; ++kb)
+            for (m = m0; m < m1; ++m)
+                for (n = n0; n < n1; ++n) {
+                    double p = block_dot(xd + m * K + kb * 128, wd + n * K + kb * 128);
+                    int64_t wrow = ws_of_col ? n : n / 128;
+                    y[m * N + n] += ((double)xs[m * KB + kb] * (double)ws[wrow * KB + kb]) * ldexp(p, -18);
+                }
+    }
+}
+
+/* Work arrays for the decoded operands; 0 on success, -1 if out of memory. */
+static int gemm_full(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
+                     int64_t K, int ws_of_col, double *y)
+{
+    double *xd = (double *)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    double *wd = (double *)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(double));
+    if (!xd || !wd) {
+        free(xd);
+        free(wd);
+        return -1;
+    }
+    build_e4m3_x512_table();
+    decode_x512(xq, M * K, xd);
+    decode_x512(wq, N * K, wd);
+    gemm_rows_decoded(xd, xs, wd, ws, 0, M, N, K, ws_of_col, y);
+    free(xd);
+    free(wd);
+    return 0;
+}
+
+/* oracle_gemm, every output, bit-identical. */
+int oracle_gemm_full(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
+                     int64_t K, double *y)
+{
+    return gemm_full(xq, xs, wq, ws, M, N, K, 0, y);
+}
+
+/* oracle_gemm_1x128, every output, bit-identical. */
+int oracle_gemm_1x128_full(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
+                           int64_t N, int64_t K, double *y)
+{
+    return gemm_full(xq, xs, wq, ws, M, N, K, 1, y);
+}
+
+/* oracle_grouped_gemm, every output, bit-identical: each run of consecutive
+ * rows that expert_of_row gives the same expert e is multiplied by expert e's
+ * weights; rows no expert contains are NaN. */
+int oracle_grouped_gemm_full(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                             const int32_t *offs, int64_t E, int64_t M_total, int64_t N, int64_t K, double *y)
+{
+    int64_t wstride = N * K, sstride = (N / 128) * (K / 128), b, t, n, decoded = -1;
+    double *xd = (double *)malloc((size_t)(M_total * K > 0 ? M_total * K : 1) * sizeof(double));
+    double *wd = (double *)malloc((size_t)(wstride > 0 ? wstride : 1) * sizeof(double));
+    if (!xd || !wd) {
+        free(xd);
+        free(wd);
+        return -1;
+    }
+    build_e4m3_x512_table();
+    decode_x512(xq, M_total * K, xd);
+    for (b = 0; b < M_total; b = t) {
+        int64_t e = expert_of_row(offs, E, b);
+        for (t = b + 1; t < M_total && expert_of_row(offs, E, t) == e; ++t)
+            ;
+        if (e < 0) {
+            for (n = b * N; n < t * N; ++n)
+                y[n] = NAN;
+            continue;
+        }
+        if (e != decoded) {
+            decode_x512(wq + e * wstride, wstride, wd);
+            decoded = e;
+        }
+        gemm_rows_decoded(xd, xs, wd, ws + e * sstride, b, t, N, K, 0, y);
+    }
+    free(xd);
+    free(wd);
+    return 0;
 }
 
 /* ---- threading ------------------------------------------------------------- */

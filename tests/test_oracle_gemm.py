@@ -187,3 +187,91 @@ def test_routing_counts():
     for e in range(0, 128, 17):
         seg = row_token[offs[e]:offs[e + 1]]
         assert (np.diff(seg) > 0).all()
+
+
+# ---- the full-output GEMMs (codes decoded once, block sums in fp64) ---------------
+
+def test_full_gemm_table_is_decode_times_512(orc):
+    """Every entry of the full-output GEMMs' table is decode(c) * 2^9: an integer of
+    magnitude <= 229376 for the 254 finite codes, NaN for 0x7F and 0xFF."""
+    t = orc.e4m3_x512_table()
+    for c in range(256):
+        d = orc.e4m3_decode(c)
+        if c in (0x7F, 0xFF):
+            assert np.isnan(t[c]) and np.isnan(d)
+        else:
+            assert t[c] == d * 512.0 and t[c] == np.round(t[c]) and abs(t[c]) <= 229376
+    assert t[0x7E] == 448 * 512 and t[0x01] == 1 and t[0x38] == 512 and t[0x80] == 0
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 512), (1, 128, 128), (17, 256, 384), (130, 384, 1024), (9, 128, 2048)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_full_gemm_bit_identical_to_elementwise(orc, shape, mode):
+    """gemm_full computes the same fp64 numbers as gemm, bit for bit (each block sum
+    is exact in both; the scale products and the ascending sum over blocks are the
+    same operations)."""
+    M, N, K = shape
+    xq, xs, wq, ws = _operands(orc, M, N, K, seed=M * 3 + K, mode=mode)
+    a = orc.gemm(xq, xs, wq, ws)
+    b = orc.gemm_full(xq, xs, wq, ws)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    # and the closed form holds for it directly
+    ref = _dequant_rows(orc, xq, xs) @ _dequant_tiles(orc, wq, ws).T
+    assert np.max(np.abs(b - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2)) * np.sqrt(K)
+
+
+def test_full_gemm_extreme_codes_exact(orc):
+    """Blocks of +-448 codes (the largest products, 128 * 448^2 per block) and of the
+    smallest subnormal: the fp64 block sums stay exact, so unit scales give the exact
+    integer result."""
+    M, N, K = 4, 128, 256
+    xq = np.full((M, K), 0x7E, np.uint8)
+    xq[1] = 0xFE
+    xq[2] = 0x01
+    xq[3, :128] = 0x7E
+    xq[3, 128:] = 0x81
+    wq = np.full((N, K), 0x7E, np.uint8)
+    wq[::2] = 0x01
+    xs = np.ones((M, K // 128), np.float32)
+    ws = np.ones((N // 128, K // 128), np.float32)
+    y = orc.gemm_full(xq, xs, wq, ws)
+    big, tiny = 448.0, 2.0 ** -9
+    assert y[0, 1] == K * big * big and y[1, 1] == -K * big * big
+    assert y[0, 0] == K * big * tiny and y[2, 0] == K * tiny * tiny
+    assert y[3, 1] == 128 * big * big - 128 * tiny * big
+    assert np.array_equal(y.view(np.uint64), orc.gemm(xq, xs, wq, ws).view(np.uint64))
+
+
+def test_full_gemm_1x128_bit_identical(orc):
+    M, N, K = 70, 256, 384
+    g = np.random.default_rng(11)
+    xq = g.integers(0, 256, (M, K), dtype=np.uint8)
+    wq = g.integers(0, 256, (N, K), dtype=np.uint8)
+    xq[xq & 0x7F == 0x7F] = 0x10
+    wq[wq & 0x7F == 0x7F] = 0x10
+    xs = g.uniform(0.5, 2, (M, K // 128)).astype(np.float32)
+    ws = g.uniform(0.5, 2, (N, K // 128)).astype(np.float32)
+    a = orc.gemm_1x128(xq, xs, wq, ws)
+    b = orc.gemm_1x128_full(xq, xs, wq, ws)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+@pytest.mark.parametrize("offs", [[0, 5, 5, 134, 135, 199, 300], [0, 0, 0, 7], [0, 128, 256, 512],
+                                  [0, 10, 3, 20, 40], [0, 10, 20, 15, 40]],
+                         ids=["ragged", "leading_empty", "aligned", "malformed_dip", "malformed_overlap"])
+def test_full_grouped_bit_identical(orc, offs):
+    """grouped_gemm_full matches grouped_gemm bit for bit, including which expert
+    owns each row when the offsets are not monotone, and NaN rows that no expert owns."""
+    E, N, K = len(offs) - 1, 256, 384
+    M = max(offs)
+    offs = np.array(offs, np.int32)
+    x = synth.activations(M, K, seed=3)
+    w = synth.expert_weights(E, N, K, seed=3, sub=synth.SUB_W)
+    xq, xs = orc.quant_act_1x128(x)
+    wq, ws = orc.quant_w_128x128(w.reshape(E * N, K))
+    wq, ws = wq.reshape(E, N, K), ws.reshape(E, N // 128, K // 128)
+    a = orc.grouped_gemm(xq, xs, wq, ws, offs)
+    b = orc.grouped_gemm_full(xq, xs, wq, ws, offs)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    ok = ~np.isnan(a)
+    assert np.array_equal(a[ok].view(np.uint64), b[ok].view(np.uint64))
