@@ -61,15 +61,19 @@ def gemm_gate(name, y_gpu: np.ndarray, y_ref: np.ndarray, tol: float = GEMM_TOL)
 
 
 def sample_positions(M, N, count, seed=0, block=128):
-    """Output positions for sampled checks: every corner and tile edge, then random."""
+    """Output positions for sampled checks: every corner, the full mesh of tile-edge
+    rows x tile-edge columns (the first and last row and column of every 128-wide
+    tile), one random position inside every 128x128 tile, then `count` random ones."""
     g = np.random.default_rng(seed)
     edge_r = sorted({0, M - 1} | {min(M - 1, r) for k in range(1, M // block + 1) for r in (k * block - 1, k * block)})
     edge_c = sorted({0, N - 1} | {min(N - 1, c) for k in range(1, N // block + 1) for c in (k * block - 1, k * block)})
-    er = np.array(edge_r[:: max(1, len(edge_r) // 64)], dtype=np.int64)
-    ec = np.array(edge_c[:: max(1, len(edge_c) // 64)], dtype=np.int64)
-    rr, cc = np.meshgrid(er, ec[:16], indexing="ij")
-    rows = [rr.reshape(-1), g.integers(0, M, count)]
-    cols = [cc.reshape(-1), g.integers(0, N, count)]
+    rr, cc = np.meshgrid(np.array(edge_r, np.int64), np.array(edge_c, np.int64), indexing="ij")
+    tr, tc = np.meshgrid(np.arange(0, M, block, dtype=np.int64), np.arange(0, N, block, dtype=np.int64),
+                         indexing="ij")
+    tr = np.minimum(tr + g.integers(0, block, tr.shape), M - 1)
+    tc = np.minimum(tc + g.integers(0, block, tc.shape), N - 1)
+    rows = [rr.reshape(-1), tr.reshape(-1), g.integers(0, M, count)]
+    cols = [cc.reshape(-1), tc.reshape(-1), g.integers(0, N, count)]
     return np.concatenate(rows), np.concatenate(cols)
 
 

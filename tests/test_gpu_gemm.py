@@ -5,8 +5,8 @@ multiplies with the library; the oracle quantizes and multiplies with its own
 code.  Gate (fp32 output mode): max |Y_gpu - Y_oracle| <= 1e-2 * rms(Y_oracle).
 The bf16 output must equal the round-to-nearest-even of the fp32 output bit
 for bit.  Shapes: the tiny layer, ragged shapes that leave partial tiles, the
-8B-shaped dense layers and the decode shapes at full size (sampled outputs),
-and the MoE layer.
+8B-shaped dense layers, the decode grid and the MoE layer at full size
+(every output, against the oracle's full-output GEMMs).
 """
 
 import numpy as np
@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import assert_bitexact, bf16_to_dev, gemm_gate, host, sample_positions, say, to_dev
+from gpu_util import assert_bitexact, bf16_to_dev, gemm_gate, host, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -123,12 +123,13 @@ def test_gemm_empty(fp8bs):
     assert y.shape == (0, 128)
 
 
-# 8B-shaped dense layers (M = 8192) and decode shapes, full size, sampled outputs
+# 8B-shaped dense layers (M = 8192) and the decode grid (M in {1, 16, 64, 256} against the
+# gate+up and down weights), full size, every output
 LARGE = [
     ("qkv", 8192, 6144, 4096), ("gate_up", 8192, 28672, 4096), ("down", 8192, 4096, 14336),
     ("o_proj", 8192, 4096, 4096),
-    ("decode1_gate_up", 1, 28672, 4096), ("decode1_down", 1, 4096, 14336), ("decode16_down", 16, 4096, 14336),
-    ("decode64_gate_up", 64, 28672, 4096), ("decode256_down", 256, 4096, 14336),
+] + [("decode%d_%s" % (m, name), m, n, k) for m in (1, 16, 64, 256)
+     for name, n, k in (("gate_up", 28672, 4096), ("down", 4096, 14336))] + [
     # one K block per tile and more tiles than workgroups: every workgroup walks several one-step tiles
     ("k128_many_tiles", 4352, 4096, 128),
 ]
@@ -136,24 +137,23 @@ LARGE = [
 
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("case", LARGE, ids=lambda c: c[0])
-def test_gemm_parity_full_size_sampled(fp8bs, orc, case, mode):
+def test_gemm_parity_full_size(fp8bs, orc, case, mode):
     name, M, N, K = case
-    if mode == 1 and not name.startswith(("qkv", "decode", "k128")):
-        pytest.skip("POW2 at full size is covered on qkv, the decode shapes and the K=128 case")
     say("fp8_block_gemm %s M=%d N=%d K=%d mode=%d" % (name, M, N, K, mode))
     x, w, xd, wd, xq, xs, wq, ws, y32, y16, ((xq_r, xs_r), (wq_r, ws_r)) = _run_pair(fp8bs, orc, M, N, K, mode)
     assert_bitexact("xq", host(xq), xq_r)
     assert_bitexact("xs", host(xs), xs_r)
     assert_bitexact("wq", host(wq), wq_r)
     assert_bitexact("ws", host(ws), ws_r)
-    rows, cols = sample_positions(M, N, 3000, seed=M + N + K)
-    ref = orc.gemm_sampled(xq_r, xs_r, wq_r, ws_r, rows, cols)
-    y = host(y32)[rows, cols]
-    gemm_gate("Y fp32 (sampled %d)" % rows.size, y, ref)
+    del x, w, xd, wd
+    ref = orc.gemm_full(xq_r, xs_r, wq_r, ws_r)
+    gemm_gate("Y fp32 (all %d outputs)" % ref.size, host(y32), ref)
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    del y16
     if mode == 1:
-        yp = host(_pow2_outputs(fp8bs.fp8_block_gemm_pow2, xq, xs, wq, ws))[rows, cols]
-        gemm_gate("Y fp32 (pow2 entry, sampled %d)" % rows.size, yp, ref)
+        del y32
+        gemm_gate("Y fp32 (pow2 entry, all %d outputs)" % ref.size,
+                  host(_pow2_outputs(fp8bs.fp8_block_gemm_pow2, xq, xs, wq, ws)), ref)
 
 
 # ---- grouped (MoE) ---------------------------------------------------------------
@@ -210,10 +210,8 @@ def test_grouped_parity(fp8bs, orc, counts, mode):
 
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
-def test_grouped_parity_moe_full_size_sampled(fp8bs, orc, proj, mode):
-    """128 experts, hidden 2048, expert FFN 768, 8192 tokens routed top-8."""
-    if mode == 1 and proj == "down":
-        pytest.skip("POW2 at full MoE size is covered on gate_up")
+def test_grouped_parity_moe_full_size(fp8bs, orc, proj, mode):
+    """128 experts, hidden 2048, expert FFN 768, 8192 tokens routed top-8; every output."""
     row_token, offs = synth.moe_routing(8192, 128, 8)
     counts = np.diff(offs)
     if proj == "gate_up":
@@ -225,10 +223,9 @@ def test_grouped_parity_moe_full_size_sampled(fp8bs, orc, proj, mode):
         args = {}
     say("fp8_block_grouped_gemm MoE %s M=%d N=%d K=%d mode=%d" % (proj, offs[-1], N, K, mode))
     xq_r, xs_r, wq_r, ws_r, offs, y32, y16 = _grouped(fp8bs, orc, counts, N, K, mode, **args)
-    rows, cols = sample_positions(int(offs[-1]), N, 4000, seed=N)
-    ref = orc.grouped_gemm_sampled(xq_r, xs_r, wq_r, ws_r, offs, rows, cols)
+    ref = orc.grouped_gemm_full(xq_r, xs_r, wq_r, ws_r, offs)
     if mode == 1:
         y32, yp = y32
-        gemm_gate("Y fp32 (pow2 entry, sampled %d)" % rows.size, host(yp)[rows, cols], ref)
-    gemm_gate("Y fp32 (sampled %d)" % rows.size, host(y32)[rows, cols], ref)
+        gemm_gate("Y fp32 (pow2 entry, all %d outputs)" % ref.size, host(yp), ref)
+    gemm_gate("Y fp32 (all %d outputs)" % ref.size, host(y32), ref)
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
