@@ -153,6 +153,57 @@ def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+_CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _out(t, shape, dtypes, device, name) -> torch.Tensor:
+    """A caller-provided output: the C ABI receives no output sizes, so the
+    kernels would write past an undersized or mistyped buffer; check it here."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s must have dtype %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _pair_out(out, M, K, device, nq="xq", ns="xs"):
+    """(codes [M, K], scales [M, K/128]) outputs of a 1x128 quantizer."""
+    if out is None:
+        return (torch.empty((M, K), dtype=torch.uint8, device=device),
+                torch.empty((M, K // 128), dtype=torch.float32, device=device))
+    if len(out) != 2:
+        raise ValueError("out must be a pair (codes, scales)")
+    return (_out(out[0], (M, K), _CODE_DTYPES, device, "out[0] (%s)" % nq),
+            _out(out[1], (M, K // 128), (torch.float32,), device, "out[1] (%s)" % ns))
+
+
+def _same_device(device, *named):
+    for name, t in named:
+        if t.device != device:
+            raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+
+
+def _workspace(workspace, need, device):
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    return workspace
+
+
+def _y_out(out, M, N, code, device):
+    dt = torch.bfloat16 if code == OUT_BF16 else torch.float32
+    if out is None:
+        return torch.empty((M, N), dtype=dt, device=device)
+    return _out(out, (M, N), (dt,), device, "out")
+
+
 # ---- quantizers ----------------------------------------------------------------
 
 def quant_act_1x128(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
@@ -161,11 +212,7 @@ def quant_act_1x128(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
-    if out is None:
-        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-        xs = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
-    else:
-        xq, xs = out
+    xq, xs = _pair_out(out, M, K, x.device)
     _check("quant_act_1x128", lib().quant_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(xs), int(mode), _stream(x)))
     return xq, xs
 
@@ -180,11 +227,7 @@ def quant_act_1x128_gather(x: torch.Tensor, rows: torch.Tensor, mode: int = SCAL
         raise ValueError("rows must be a contiguous 1-D int32 tensor on x's device")
     T, K = x.shape
     M = rows.shape[0]
-    if out is None:
-        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-        xs = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
-    else:
-        xq, xs = out
+    xq, xs = _pair_out(out, M, K, x.device)
     _check("quant_act_1x128_gather", lib().quant_act_1x128_gather(_ptr(x), T, K, _ptr(rows), M, _ptr(xq), _ptr(xs),
                                                                  int(mode), _stream(x)))
     return xq, xs
@@ -197,11 +240,7 @@ def swiglu_quant_1x128(gu: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     if gu.dim() != 2 or gu.shape[1] % 2:
         raise ValueError("gu must be 2-D [M, 2F]")
     M, F = gu.shape[0], gu.shape[1] // 2
-    if out is None:
-        hq = torch.empty((M, F), dtype=torch.uint8, device=gu.device)
-        hs = torch.empty((M, F // 128), dtype=torch.float32, device=gu.device)
-    else:
-        hq, hs = out
+    hq, hs = _pair_out(out, M, F, gu.device, "hq", "hs")
     _check("swiglu_quant_1x128", lib().swiglu_quant_1x128(_ptr(gu), M, F, _ptr(hq), _ptr(hs), int(mode), _stream(gu)))
     return hq, hs
 
@@ -212,11 +251,7 @@ def quant_act_1x128_t(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
-    if out is None:
-        xqt = torch.empty((K, M), dtype=torch.uint8, device=x.device)
-        xst = torch.empty((K, M // 128), dtype=torch.float32, device=x.device)
-    else:
-        xqt, xst = out
+    xqt, xst = _pair_out(out, K, M, x.device, "xqt", "xst")
     _check("quant_act_1x128_t", lib().quant_act_1x128_t(_ptr(x), M, K, _ptr(xqt), _ptr(xst), int(mode), _stream(x)))
     return xqt, xst
 
@@ -228,12 +263,10 @@ def quant_act_1x128_dual(x: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
-    if out is None:
-        out = (torch.empty((M, K), dtype=torch.uint8, device=x.device),
-               torch.empty((M, K // 128), dtype=torch.float32, device=x.device),
-               torch.empty((K, M), dtype=torch.uint8, device=x.device),
-               torch.empty((K, M // 128), dtype=torch.float32, device=x.device))
-    xq, xs, xqt, xst = out
+    if out is not None and len(out) != 4:
+        raise ValueError("out must be (xq, xs, xqt, xst)")
+    xq, xs = _pair_out(None if out is None else out[:2], M, K, x.device)
+    xqt, xst = _pair_out(None if out is None else out[2:], K, M, x.device, "xqt", "xst")
     _check("quant_act_1x128_dual", lib().quant_act_1x128_dual(_ptr(x), M, K, _ptr(xq), _ptr(xs), _ptr(xqt),
                                                               _ptr(xst), int(mode), _stream(x)))
     return xq, xs, xqt, xst
@@ -245,11 +278,7 @@ def quant_w_128x128(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     if w.dim() != 2:
         raise ValueError("w must be 2-D [N, K]")
     N, K = w.shape
-    if out is None:
-        wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
-        ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
-    else:
-        wq, ws = out
+    wq, ws = _w_out(out, w)
     _check("quant_w_128x128", lib().quant_w_128x128(_ptr(w), N, K, _ptr(wq), _ptr(ws), int(mode), _stream(w)))
     return wq, ws
 
@@ -260,10 +289,10 @@ def quant_w_128x128_batched(ws_in: Sequence[torch.Tensor], mode: int = SCALE_EXA
     if n == 0:
         return []
     tensors = [_bf16_payload(w, "w[%d]" % i) for i, w in enumerate(ws_in)]
-    if outs is None:
-        outs = [(torch.empty(w.shape, dtype=torch.uint8, device=w.device),
-                 torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32, device=w.device))
-                for w in tensors]
+    _batch_devices(tensors)
+    if outs is not None and len(outs) != n:
+        raise ValueError("outs must hold one (codes, scales) pair per weight")
+    outs = [_w_out(None if outs is None else outs[i], w) for i, w in enumerate(tensors)]
     arr_p = ctypes.c_void_p * n
     arr_i = ctypes.c_int64 * n
     wp = arr_p(*[w.data_ptr() for w in tensors])
@@ -278,12 +307,36 @@ def quant_w_128x128_batched(ws_in: Sequence[torch.Tensor], mode: int = SCALE_EXA
     return outs
 
 
-def _dual_outs(w: torch.Tensor):
+def _w_out(out, w: torch.Tensor):
+    """(codes [N, K], scales [N/128, K/128]) outputs of the 128x128 quantizer."""
     N, K = w.shape
-    return (torch.empty((N, K), dtype=torch.uint8, device=w.device),
-            torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device),
-            torch.empty((K, N), dtype=torch.uint8, device=w.device),
-            torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device))
+    if out is None:
+        return (torch.empty((N, K), dtype=torch.uint8, device=w.device),
+                torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device))
+    if len(out) != 2:
+        raise ValueError("out must be a pair (codes, scales)")
+    return (_out(out[0], (N, K), _CODE_DTYPES, w.device, "out[0] (wq)"),
+            _out(out[1], (N // 128, K // 128), (torch.float32,), w.device, "out[1] (ws)"))
+
+
+def _batch_devices(tensors):
+    for i, w in enumerate(tensors):
+        if w.dim() != 2:
+            raise ValueError("w[%d] must be 2-D [N, K]" % i)
+        _same_device(tensors[0].device, ("w[%d]" % i, w))
+
+
+def _dual_outs(w: torch.Tensor, out=None):
+    """(wq [N, K], ws [N/128, K/128], wqt [K, N], wst [K/128, N/128]) of the dual quantizer."""
+    N, K = w.shape
+    if out is not None and len(out) != 4:
+        raise ValueError("out must be (wq, ws, wqt, wst)")
+    wq, ws = _w_out(None if out is None else out[:2], w)
+    if out is None:
+        return (wq, ws, torch.empty((K, N), dtype=torch.uint8, device=w.device),
+                torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device))
+    return (wq, ws, _out(out[2], (K, N), _CODE_DTYPES, w.device, "out[2] (wqt)"),
+            _out(out[3], (K // 128, N // 128), (torch.float32,), w.device, "out[3] (wst)"))
 
 
 def quant_w_128x128_dual(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):
@@ -293,7 +346,7 @@ def quant_w_128x128_dual(w: torch.Tensor, mode: int = SCALE_EXACT, out=None):
     if w.dim() != 2:
         raise ValueError("w must be 2-D [N, K]")
     N, K = w.shape
-    wq, ws, wqt, wst = out if out is not None else _dual_outs(w)
+    wq, ws, wqt, wst = _dual_outs(w, out)
     _check("quant_w_128x128_dual", lib().quant_w_128x128_dual(_ptr(w), N, K, _ptr(wq), _ptr(ws), _ptr(wqt),
                                                               _ptr(wst), int(mode), _stream(w)))
     return wq, ws, wqt, wst
@@ -305,8 +358,10 @@ def quant_w_128x128_dual_batched(ws_in: Sequence[torch.Tensor], mode: int = SCAL
     if n == 0:
         return []
     tensors = [_bf16_payload(w, "w[%d]" % i) for i, w in enumerate(ws_in)]
-    if outs is None:
-        outs = [_dual_outs(w) for w in tensors]
+    _batch_devices(tensors)
+    if outs is not None and len(outs) != n:
+        raise ValueError("outs must hold one (wq, ws, wqt, wst) tuple per weight")
+    outs = [_dual_outs(w, None if outs is None else outs[i]) for i, w in enumerate(tensors)]
     arr_p = ctypes.c_void_p * n
     arr_i = ctypes.c_int64 * n
     cols = [arr_p(*[o[j].data_ptr() for o in outs]) for j in range(4)]
@@ -357,9 +412,9 @@ def fp8_block_gemm_1x128(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None):
     N = wq.shape[0]
     if wq.shape[1] != K or xs.shape != (M, K // 128) or ws.shape != (N, K // 128):
         raise ValueError("operand shapes do not match")
+    _same_device(xq.device, ("xs", xs), ("wq", wq), ("ws", ws))
     code = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=xq.device)
+    out = _y_out(out, M, N, code, xq.device)
     _check("fp8_block_gemm_1x128", lib().fp8_block_gemm_1x128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
                                                               _ptr(out), code, _stream(xq)))
     return out
@@ -372,12 +427,10 @@ def _gemm(fn, xq, xs, wq, ws, out_dtype, out, workspace):
     N = wq.shape[0]
     if wq.shape[1] != K or xs.shape != (M, K // 128) or ws.shape != (N // 128, K // 128):
         raise ValueError("operand shapes do not match")
+    _same_device(xq.device, ("xs", xs), ("wq", wq), ("ws", ws))
     code = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=xq.device)
-    need = gemm_workspace_size(M, N, K)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    out = _y_out(out, M, N, code, xq.device)
+    workspace = _workspace(workspace, gemm_workspace_size(M, N, K), xq.device)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code,
                             _ptr(workspace), wsz, _stream(xq))
@@ -408,12 +461,10 @@ def _linear(fn, x, wq, ws, out_dtype, out, workspace):
     N = wq.shape[0]
     if wq.shape[1] != K or ws.shape != (N // 128, K // 128):
         raise ValueError("operand shapes do not match")
+    _same_device(x.device, ("wq", wq), ("ws", ws))
     code = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=x.device)
-    need = linear_workspace_size(M, N, K)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    out = _y_out(out, M, N, code, x.device)
+    workspace = _workspace(workspace, linear_workspace_size(M, N, K), x.device)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = getattr(lib(), fn)(_ptr(x), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code, _ptr(workspace), wsz, _stream(x))
     _check(fn, st)
@@ -433,18 +484,18 @@ def fp8_block_grouped_gemm_pow2(xq, xs, wq, ws, group_offsets, out_dtype=torch.b
 def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace):
     xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
     xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
-    if group_offsets.dtype != torch.int32 or not group_offsets.is_cuda:
-        raise ValueError("group_offsets must be an int32 device tensor")
+    if group_offsets.dtype != torch.int32 or not group_offsets.is_cuda or not group_offsets.is_contiguous():
+        raise ValueError("group_offsets must be a contiguous int32 device tensor")
+    if xq.dim() != 2 or wq.dim() != 3:
+        raise ValueError("xq must be [M_total, K] and wq [E, N, K]")
     M, K = xq.shape
     E, N, K2 = wq.shape
     if K2 != K or xs.shape != (M, K // 128) or ws.shape != (E, N // 128, K // 128) or group_offsets.numel() != E + 1:
         raise ValueError("operand shapes do not match")
+    _same_device(xq.device, ("xs", xs), ("wq", wq), ("ws", ws), ("group_offsets", group_offsets))
     code = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16 if code == OUT_BF16 else torch.float32, device=xq.device)
-    need = grouped_workspace_size(E, M, N, K)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    out = _y_out(out, M, N, code, xq.device)
+    workspace = _workspace(workspace, grouped_workspace_size(E, M, N, K), xq.device)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(group_offsets), E, M, N, K,
                             _ptr(out), code, _ptr(workspace), wsz, _stream(xq))
