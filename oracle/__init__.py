@@ -73,6 +73,7 @@ def lib():
             f.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.oracle_grouped_gemm_full.restype = ctypes.c_int
         L.oracle_grouped_gemm_full.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+        L.oracle_kv_attention_decode.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -331,3 +332,24 @@ def grouped_gemm_full(xq, xs, wq, ws, offsets) -> np.ndarray:
                                       _ptr(y)) != 0:
         raise MemoryError("oracle: no memory for the decoded operands")
     return y
+
+
+# ---- attention over an FP8 KV cache ---------------------------------------------
+
+def kv_attention_decode(q_bf16, kq, ks, vq, vs, lens, sm_scale: float) -> np.ndarray:
+    """fp64 o [B, Hq, 128]: one query token per sequence attending to its first lens[b]
+    cached tokens; q bf16 payloads [B, Hq, 128], kq / vq codes [B, T, Hkv, 128], ks / vs
+    fp32 [B, T, Hkv], lens int32 [B]."""
+    q = _c(q_bf16, np.uint16)
+    kq, vq = _c(kq, np.uint8), _c(vq, np.uint8)
+    ks, vs = _c(ks, np.float32), _c(vs, np.float32)
+    lens = _c(np.asarray(lens, dtype=np.int32), np.int32)
+    B, Hq, D = q.shape
+    _, T, Hkv, D2 = kq.shape
+    if D != 128 or D2 != 128 or Hq % Hkv or vq.shape != kq.shape or ks.shape != (B, T, Hkv) or \
+            vs.shape != ks.shape or lens.shape != (B,):
+        raise ValueError("shapes do not match")
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    lib().oracle_kv_attention_decode(_ptr(q), _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _ptr(lens), B, T, Hq, Hkv,
+                                     float(sm_scale), _ptr(out))
+    return out
