@@ -29,6 +29,8 @@ SCALE_EXACT = 0
 SCALE_POW2 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
+STATUS_SCRATCH_TOO_SMALL = 6
+NOALLOC_SCRATCH_BYTES = 1 << 20  # FP8BS_NOALLOC_SCRATCH_BYTES
 
 # The functions declared in include/fp8bs.h, in declaration order.
 EXPORTS = (
@@ -46,6 +48,7 @@ EXPORTS = (
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_pow2",
     "fp8_block_grouped_gemm_pow2",
+    "fp8_block_grouped_gemm_noalloc",
     "fp8_block_linear",
     "fp8_block_linear_pow2",
     "fp8bs_linear_workspace_size",
@@ -86,6 +89,7 @@ def lib() -> ctypes.CDLL:
         L.fp8_block_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_gemm_pow2.argtypes = L.fp8_block_gemm.argtypes
         L.fp8_block_grouped_gemm_pow2.argtypes = L.fp8_block_grouped_gemm.argtypes
+        L.fp8_block_grouped_gemm_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
         L.fp8_block_linear.argtypes = [P, P, P, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_linear_pow2.argtypes = L.fp8_block_linear.argtypes
         L.fp8bs_linear_workspace_size.argtypes = [I64, I64, I64]
@@ -102,6 +106,7 @@ def lib() -> ctypes.CDLL:
                    "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
+                   "fp8_block_grouped_gemm_noalloc",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
             getattr(L, fn).restype = I32
         _lib = L
@@ -481,7 +486,15 @@ def fp8_block_grouped_gemm_pow2(xq, xs, wq, ws, group_offsets, out_dtype=torch.b
     return _grouped("fp8_block_grouped_gemm_pow2", xq, xs, wq, ws, group_offsets, out_dtype, out, workspace)
 
 
-def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace):
+def fp8_block_grouped_gemm_noalloc(xq, xs, wq, ws, group_offsets, out_dtype=torch.bfloat16, out=None):
+    """fp8_block_grouped_gemm whose library call allocates nothing: its row-tile tables live in
+    the library's static device array (calls overlapping in time on one GPU race on it).  Pass
+    `out` to keep this call free of allocations on the Python side too."""
+    return _grouped("fp8_block_grouped_gemm_noalloc", xq, xs, wq, ws, group_offsets, out_dtype, out, None,
+                    noalloc=True)
+
+
+def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace, noalloc=False):
     xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
     xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
     if group_offsets.dtype != torch.int32 or not group_offsets.is_cuda or not group_offsets.is_contiguous():
@@ -495,6 +508,11 @@ def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace):
     _same_device(xq.device, ("xs", xs), ("wq", wq), ("ws", ws), ("group_offsets", group_offsets))
     code = _out_code(out_dtype)
     out = _y_out(out, M, N, code, xq.device)
+    if noalloc:
+        st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(group_offsets), E, M, N, K,
+                                _ptr(out), code, _stream(xq))
+        _check(fn, st)
+        return out
     workspace = _workspace(workspace, grouped_workspace_size(E, M, N, K), xq.device)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(group_offsets), E, M, N, K,

@@ -109,6 +109,9 @@ const char *fp8bs_status_string(int status)
         return "workspace too small";
     case FP8BS_HIP_ERROR:
         return "HIP runtime error at launch";
+    case FP8BS_SCRATCH_TOO_SMALL:
+        return "the problem needs more scratch than the library's static device buffer holds "
+               "(fp8_block_grouped_gemm_noalloc: use fp8_block_grouped_gemm with a workspace)";
     default:
         return "unknown status";
     }
@@ -364,7 +367,8 @@ static int gemm_impl(const void *xq, const float *xs, const void *wq, const floa
 
 static int grouped_impl(const void *xq, const float *xs, const void *wq, const float *ws,
                         const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
-                        int out_dtype, int pow2, void *workspace, size_t workspace_bytes, void *stream)
+                        int out_dtype, int pow2, void *workspace, size_t workspace_bytes, void *stream,
+                        bool noalloc = false)
 {
     int st = check_gemm_common(xq, xs, y, M_total, N, K, out_dtype);
     if (st != FP8BS_OK)
@@ -379,15 +383,26 @@ static int grouped_impl(const void *xq, const float *xs, const void *wq, const f
     if ((M_total + 127) / 128 + E >= kMaxDim / (N / 128))
         return FP8BS_UNSUPPORTED_SHAPE;
     const size_t need = fp8bs::grouped_workspace_size(E, M_total, N, K);
-    if (workspace_bytes < need)
-        return FP8BS_WORKSPACE_TOO_SMALL;
-    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
-        return FP8BS_INVALID_ARG;
+    if (noalloc) {
+        if (need > FP8BS_NOALLOC_SCRATCH_BYTES)
+            return FP8BS_SCRATCH_TOO_SMALL;
+    } else {
+        if (workspace_bytes < need)
+            return FP8BS_WORKSPACE_TOO_SMALL;
+        if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+            return FP8BS_INVALID_ARG;
+    }
     if ((st = check_device()) != FP8BS_OK)
         return st;
+    // the no-allocation form: the tables go to the library's static device array
+    if (noalloc && need > 0 && fp8bs::noalloc_scratch(&workspace) != hipSuccess)
+        return FP8BS_HIP_ERROR;
     return status_of(fp8bs::launch_grouped_gemm(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y,
                                                 out_dtype == FP8BS_OUT_FP32, pow2, workspace, (hipStream_t)stream));
 }
+
+static_assert(FP8BS_NOALLOC_SCRATCH_BYTES == fp8bs::kNoallocScratchBytes,
+              "the header's scratch size must be the library's");
 
 size_t fp8bs_linear_workspace_size(int64_t M, int64_t N, int64_t K)
 {
@@ -464,6 +479,13 @@ int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const void *wq,
 {
     return grouped_impl(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y, out_dtype, 1, workspace, workspace_bytes,
                         stream);
+}
+
+int fp8_block_grouped_gemm_noalloc(const void *xq, const float *xs, const void *wq, const float *ws,
+                                   const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                   void *y, int out_dtype, void *stream)
+{
+    return grouped_impl(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y, out_dtype, 0, nullptr, 0, stream, true);
 }
 
 } // extern "C"

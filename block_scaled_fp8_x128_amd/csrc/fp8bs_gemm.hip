@@ -50,6 +50,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace fp8bs {
@@ -1721,6 +1722,41 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
     a.tiles_m = (int)((M_total + 127) / 128 + E);
     a.tiles_n = (int)(N / 128);
     return run_simple<128, 128, 2, 2, true>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
+}
+
+// ---- the grouped GEMM's row-tile tables without a caller workspace ----------
+// For callers that cannot allocate (graph capture, serving loops): the tables
+// live in this file-scope device array, one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices];
+} // namespace
+
+hipError_t noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+            return e;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 } // namespace fp8bs

@@ -88,5 +88,10 @@ size_t grouped_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void *y,
                                int out_fp32, int pow2, void *workspace, hipStream_t stream);
+// Size of the library's static device array that stands in for the grouped
+// workspace in fp8_block_grouped_gemm_noalloc, and its device address on the
+// current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
+hipError_t noalloc_scratch(void **ptr);
 
 } // namespace fp8bs

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 1
+#define FP8BS_ABI_VERSION 2
 
 /* Symbols of this header are the only ones the shared library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -61,7 +61,9 @@ enum fp8bs_status {
     FP8BS_UNSUPPORTED_SHAPE = 2,   /* K (or N where required) not a multiple of 128; size too large */
     FP8BS_UNSUPPORTED_DEVICE = 3,  /* the current HIP device is not a gfx950 */
     FP8BS_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the size the query function returns */
-    FP8BS_HIP_ERROR = 5            /* the HIP runtime refused a launch */
+    FP8BS_HIP_ERROR = 5,           /* the HIP runtime refused a launch */
+    FP8BS_SCRATCH_TOO_SMALL = 6    /* fp8_block_grouped_gemm_noalloc: the problem's row-tile tables
+                                      exceed FP8BS_NOALLOC_SCRATCH_BYTES */
 };
 
 /* scale_mode */
@@ -345,6 +347,36 @@ FP8BS_API int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const
                                           const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N,
                                           int64_t K, void *y, int out_dtype, void *workspace,
                                           size_t workspace_bytes, void *stream);
+
+/*
+ * fp8_block_grouped_gemm_noalloc -- fp8_block_grouped_gemm for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace and calls no
+ * hipMalloc, hipFree or other allocating routine.
+ *
+ * Arguments, layouts and results are those of fp8_block_grouped_gemm (EXACT
+ * scales; the output is bit-identical to it).  The row-tile tables that
+ * fp8_block_grouped_gemm writes into its workspace go instead to a static
+ * device array of FP8BS_NOALLOC_SCRATCH_BYTES inside the library: one per
+ * GPU, allocated when the library's code is loaded on that GPU and held until
+ * the process ends.  Its address is looked up on the first call on each
+ * device.  The tables are rewritten in full by every call, so nothing needs
+ * clearing between calls.
+ * Concurrency: every call on one GPU shares that GPU's array.  Calls that
+ *   overlap in time on one GPU (different streams, or different host threads
+ *   without ordering) race on it and give unspecified results; serialize them,
+ *   e.g. on one stream.
+ * Limit: the tables take 16 + 16 * (ceil(M_total / 256) + 2 E) bytes, i.e.
+ *   fp8bs_grouped_workspace_size(E, M_total, N, K); about 65,500 row tiles fit
+ *   (for instance M_total = 16M rows with E = 128).
+ * Errors: as fp8_block_grouped_gemm, plus FP8BS_SCRATCH_TOO_SMALL (nothing
+ *   launched) when the tables would exceed the array, and FP8BS_HIP_ERROR if
+ *   the runtime cannot give the array's address.
+ */
+#define FP8BS_NOALLOC_SCRATCH_BYTES 1048576
+FP8BS_API int fp8_block_grouped_gemm_noalloc(const void *xq, const float *xs, const void *wq, const float *ws,
+                                             const int32_t *group_offsets, int64_t E, int64_t M_total, int64_t N,
+                                             int64_t K, void *y, int out_dtype, void *stream);
 
 /*
  * fp8_block_linear, fp8_block_linear_pow2 -- the whole FP8 linear layer from

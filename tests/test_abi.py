@@ -49,8 +49,8 @@ def test_library_exports_every_declared_symbol(fp8bs):
 
 
 def test_version_and_status_strings(fp8bs):
-    assert fp8bs.abi_version() == 1
-    for st in range(6):
+    assert fp8bs.abi_version() == 2
+    for st in range(7):
         s = fp8bs.status_string(st)
         assert isinstance(s, str) and len(s) > 1
     assert fp8bs.status_string(99) == "unknown status"
@@ -210,6 +210,27 @@ def test_gemm_validation(fp8bs):
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 128, FAKE, 0, NULL, 0, NULL) == 2    # N % 128
     assert gg(NULL, NULL, FAKE, FAKE, FAKE, 4, 0, 128, 128, NULL, 0, NULL, 0, NULL) == 0   # empty
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 256, FAKE, 0, NULL, 0, NULL) == 4   # no table space
+
+
+def test_grouped_noalloc_validation(fp8bs):
+    """fp8_block_grouped_gemm_noalloc: the grouped GEMM's checks, no workspace argument, and
+    SCRATCH_TOO_SMALL (before any device call) when its row-tile tables exceed the library's
+    static array: 16 + 16 (ceil(M_total / 256) + 2 E) bytes against 1 MiB."""
+    L = fp8bs.lib()
+    gn = L.fp8_block_grouped_gemm_noalloc
+    cap = fp8bs.NOALLOC_SCRATCH_BYTES
+    assert gn(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 128, FAKE, 0, NULL) == 1     # E == 0
+    assert gn(FAKE, FAKE, FAKE, FAKE, NULL, 4, 8, 128, 128, FAKE, 0, NULL) == 1     # null offsets
+    assert gn(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 128, FAKE, 0, NULL) == 2      # N % 128
+    assert gn(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 256, FAKE, 7, NULL) == 1     # out dtype
+    assert gn(NULL, NULL, FAKE, FAKE, FAKE, 4, 0, 256, 256, NULL, 0, NULL) == 0     # empty: no-op
+    # the largest M_total that fits with E experts, and one 256-row tile more
+    for E in (1, 128):
+        m_fit = ((cap - 16) // 16 - 2 * E) * 256
+        assert L.fp8bs_grouped_workspace_size(E, m_fit, 256, 256) <= cap
+        assert L.fp8bs_grouped_workspace_size(E, m_fit + 1, 256, 256) > cap
+        assert gn(FAKE, FAKE, FAKE, FAKE, FAKE, E, m_fit + 1, 256, 256, FAKE, 0, NULL) == 6
+    assert "scratch" in fp8bs.status_string(6)
 
 
 def test_linear_workspace_and_validation(fp8bs):
