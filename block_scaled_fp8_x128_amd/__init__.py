@@ -48,6 +48,8 @@ EXPORTS = (
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_pow2",
     "fp8_block_grouped_gemm_pow2",
+    "fp8_block_gemm_quant",
+    "fp8bs_gemm_quant_workspace_size",
     "fp8_block_grouped_gemm_noalloc",
     "fp8_block_linear",
     "fp8_block_linear_pow2",
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.fp8_block_gemm_pow2.argtypes = L.fp8_block_gemm.argtypes
         L.fp8_block_grouped_gemm_pow2.argtypes = L.fp8_block_grouped_gemm.argtypes
         L.fp8_block_grouped_gemm_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        L.fp8_block_gemm_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P, I32, P, SZ, P]
+        L.fp8bs_gemm_quant_workspace_size.argtypes = [I64, I64, I64]
+        L.fp8bs_gemm_quant_workspace_size.restype = SZ
         L.fp8_block_linear.argtypes = [P, P, P, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_linear_pow2.argtypes = L.fp8_block_linear.argtypes
         L.fp8bs_linear_workspace_size.argtypes = [I64, I64, I64]
@@ -106,7 +111,7 @@ def lib() -> ctypes.CDLL:
                    "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
-                   "fp8_block_grouped_gemm_noalloc",
+                   "fp8_block_grouped_gemm_noalloc", "fp8_block_gemm_quant",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
             getattr(L, fn).restype = I32
         _lib = L
@@ -443,6 +448,37 @@ def _gemm(fn, xq, xs, wq, ws, out_dtype, out, workspace):
     return out
 
 
+def gemm_quant_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().fp8bs_gemm_quant_workspace_size(M, N, K))
+
+
+def fp8_block_gemm_quant(xq, xs, wq, ws, mode: int = SCALE_EXACT, want_y: bool = True, out=None, workspace=None):
+    """(y bf16 [M, N] or None, yq codes [M, N], ys scales [M, N/128]): the GEMM and
+    quant_act_1x128 of its bf16 output from one call (fused into the GEMM's epilogue
+    where the shape allows).  `mode` is the scale mode of the operands and the output."""
+    xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
+    xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or xs.shape != (M, K // 128) or ws.shape != (N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    _same_device(xq.device, ("xs", xs), ("wq", wq), ("ws", ws))
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be (y or None, yq, ys)")
+        y = None if out[0] is None else _y_out(out[0], M, N, OUT_BF16, xq.device)
+        yq, ys = _pair_out(out[1:], M, N, xq.device, "yq", "ys")
+    else:
+        y = _y_out(None, M, N, OUT_BF16, xq.device) if want_y else None
+        yq, ys = _pair_out(None, M, N, xq.device, "yq", "ys")
+    workspace = _workspace(workspace, gemm_quant_workspace_size(M, N, K), xq.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_block_gemm_quant(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _ptr(yq), _ptr(ys),
+                                    int(mode), _ptr(workspace), wsz, _stream(xq))
+    _check("fp8_block_gemm_quant", st)
+    return y, yq, ys
+
+
 def linear_workspace_size(M: int, N: int, K: int) -> int:
     return int(lib().fp8bs_linear_workspace_size(M, N, K))
 
@@ -519,3 +555,4 @@ def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace, noall
                             _ptr(out), code, _ptr(workspace), wsz, _stream(xq))
     _check(fn, st)
     return out
+

@@ -488,4 +488,41 @@ int fp8_block_grouped_gemm_noalloc(const void *xq, const float *xs, const void *
     return grouped_impl(xq, xs, wq, ws, group_offsets, E, M_total, N, K, y, out_dtype, 0, nullptr, 0, stream, true);
 }
 
+size_t fp8bs_gemm_quant_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    return fp8bs::gemm_quant_workspace_size(M, N, K);
+}
+
+int fp8_block_gemm_quant(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                         int64_t K, void *y, void *yq, float *ys, int scale_mode, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    if (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2)
+        return FP8BS_INVALID_ARG;
+    int st = check_gemm_shape(M, N, K, FP8BS_OUT_BF16);
+    if (st != FP8BS_OK)
+        return st;
+    // the quantized output's scale grid [M, N/128] (as quant_act_1x128 of Y)
+    if (M * (N / 128) >= kMaxDim * 64)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (!tensor_ok(xq, M * K, 16) || !tensor_ok(xs, M * K, 4) || !tensor_ok(wq, N * K, 16) ||
+        !tensor_ok(ws, N * K, 4) || !tensor_ok(yq, M * N, 16) || !tensor_ok(ys, M * N, 4))
+        return FP8BS_INVALID_ARG;
+    if (y != nullptr && !aligned(y, 16))
+        return FP8BS_INVALID_ARG;
+    if (M == 0)
+        return FP8BS_OK;
+    const size_t need = fp8bs::gemm_quant_workspace_size(M, N, K);
+    if (workspace_bytes < need)
+        return FP8BS_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+        return FP8BS_INVALID_ARG;
+    if ((st = check_device()) != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_gemm_quant(xq, xs, wq, ws, M, N, K, y, yq, ys, scale_mode, workspace,
+                                              (hipStream_t)stream));
+}
+
 } // extern "C"

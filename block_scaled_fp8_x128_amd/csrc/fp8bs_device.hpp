@@ -185,21 +185,23 @@ struct BlockQuant {
     }
 };
 
+// 4 values (bf16 values widened to fp32) -> one dword of codes.
+template <int MODE>
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, const BlockQuant<MODE> &bq)
+{
+    if (bq.fast)
+        return pack4_e4m3(bq.q_fast(x0), bq.q_fast(x1), bq.q_fast(x2), bq.q_fast(x3));
+    const float s = bq.s;
+    return pack4_e4m3(x0 / s, x1 / s, x2 / s, x3 / s);
+}
+
 // 8 bf16 values (one 16-byte chunk) -> 8 codes.
 template <int MODE>
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, const BlockQuant<MODE> &bq)
 {
-    float x0 = bf16_lo(v.x), x1 = bf16_hi(v.x), x2 = bf16_lo(v.y), x3 = bf16_hi(v.y);
-    float x4 = bf16_lo(v.z), x5 = bf16_hi(v.z), x6 = bf16_lo(v.w), x7 = bf16_hi(v.w);
     u32x2 out;
-    if (bq.fast) {
-        out.x = pack4_e4m3(bq.q_fast(x0), bq.q_fast(x1), bq.q_fast(x2), bq.q_fast(x3));
-        out.y = pack4_e4m3(bq.q_fast(x4), bq.q_fast(x5), bq.q_fast(x6), bq.q_fast(x7));
-    } else {
-        const float s = bq.s;
-        out.x = pack4_e4m3(x0 / s, x1 / s, x2 / s, x3 / s);
-        out.y = pack4_e4m3(x4 / s, x5 / s, x6 / s, x7 / s);
-    }
+    out.x = quant4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), bq);
+    out.y = quant4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), bq);
     return out;
 }
 

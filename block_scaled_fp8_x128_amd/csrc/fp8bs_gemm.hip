@@ -102,6 +102,8 @@ struct GemmArgs {
     float *part;            // ksplit > 1: fp32 partial sums [ksplit][M][N]
     const GroupTile *gtab;  // grouped, persistent kernel: the row tiles (tiles_m entries) ...
     const int32_t *gcount;  // ... of which the first *gcount exist
+    uint8_t *yq;            // quantizing epilogue: codes [M, N] of the bf16 output ...
+    float *ys;              // ... and its 1x128 scales [M, N/128]
 };
 
 // Logical tile of workgroup `bid` (XCD-contiguous ranges, GROUP_M swizzle).
@@ -605,11 +607,17 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, T
 // operands are quantized in 1x128 blocks along the tokens): each K step's BN
 // W-row scales travel with its operands into a ring of LDS slots, and the
 // rescale forms xs * ws for each lane's 4 columns of a tile.
+// QMODE (1 = EXACT, 2 = POW2 scales): the bf16 output is also quantized in
+// 1x128 blocks along its rows, as quant_act_1x128 would quantize it, for a
+// next layer that takes FP8 input: codes to a.yq [M, N], scales to a.ys
+// [M, N/128]; the bf16 output itself is written only if a.y is not null.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, bool SPLIT, bool POW2,
-          bool WROW = false>
+          bool WROW = false, int QMODE = 0>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs args)
 {
     static_assert(!(WROW && (POW2 || GROUPED)), "per-row weight scales: dense products, VALU rescale");
+    static_assert(QMODE == 0 || (!OUT_F32 && !SPLIT && !WROW && !GROUPED && BN / WAVES_N == 128),
+                  "the quantizing epilogue: bf16 output, whole K, one 128-column block per wave");
     GemmArgs a = args;
     if constexpr (GROUPED)
         a.tiles_m = *(const CONST_AS int32_t *)a.gcount; // the tiles that exist
@@ -922,8 +930,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     auto store = [&](auto f32_tag, const uint8_t *base, const TileGeo &g) {
         constexpr bool F32 = decltype(f32_tag)::value;
         constexpr int ES = F32 ? 4 : 2;
+        const int64_t rows = g.row_end - g.row_begin;
+        const bool want_y = QMODE == 0 || base != nullptr;
         const __amdgpu_buffer_rsrc_t yr =
-            make_rsrc(base + (g.row_begin * N + g.n0) * ES, (g.row_end - g.row_begin) * N * ES);
+            make_rsrc(want_y ? base + (g.row_begin * N + g.n0) * ES : (const uint8_t *)a.yq, want_y ? rows * N * ES : 0);
         if constexpr (!F32) {
             // per 16-row tile and EPI_CW-column chunk: each lane writes its 4
             // columns of each MFMA tile into the wave's staging rows, then reads
@@ -935,18 +945,69 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             constexpr int RPI = 64 / LPR;           // rows per read-back
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
+                // the tile's bf16 values (round to nearest even), as pairs of
+                // dwords: lane l holds columns 4 (l / 16) .. + 3 of every
+                // 16-column tile j of row l % 16 (recomputed per pass: a
+                // conversion costs less than the registers of a copy)
+                auto bw_of = [&](int j) {
+                    const v4f v = acc[i][j];
+                    const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
+                    const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
+                    return u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+                };
+                if constexpr (QMODE != 0) {
+                    // Row l % 16's 128 columns of this wave are one 1x128 block of
+                    // the next layer's input, held by the four lanes l % 16 + 16 q:
+                    // amax over the lane's 32 values, then across those lanes; the
+                    // scale and codes follow the activation quantizer's encoder, so
+                    // they equal quant_act_1x128 of the bf16 output bit for bit.
+                    constexpr int QM = QMODE == 2 ? SCALE_POW2 : SCALE_EXACT;
+                    uint32_t mx = 0;
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) {
+                        const u32x2 w = bw_of(j);
+                        const uint32_t a0 = w.x & 0x7fff7fffu, a1 = w.y & 0x7fff7fffu;
+                        const uint32_t m0 = (a0 & 0xffffu) > (a0 >> 16) ? (a0 & 0xffffu) : (a0 >> 16);
+                        const uint32_t m1 = (a1 & 0xffffu) > (a1 >> 16) ? (a1 & 0xffffu) : (a1 >> 16);
+                        const uint32_t m01 = m0 > m1 ? m0 : m1;
+                        mx = mx > m01 ? mx : m01;
+                    }
+                    uint32_t o = (uint32_t)__shfl_xor((int)mx, 16);
+                    mx = mx > o ? mx : o;
+                    o = (uint32_t)__shfl_xor((int)mx, 32);
+                    mx = mx > o ? mx : o;
+                    BlockQuant<QM> bq;
+                    bq.init(amax_value(mx));
+                    // codes staged by rows (row fr: bytes 16 j + 4 fg), then read back
+                    // 16 bytes per lane, 8 lanes per 128-byte row
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) {
+                        const u32x2 w = bw_of(j);
+                        *(uint32_t *)(epi_lds + fr * C::EPI_RS + j * 16 + fg * 4) =
+                            quant4<QM>(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), bq);
+                    }
+                    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.yq + g.row_begin * N + g.n0, rows * N);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int r = h * 8 + lane / 8, cc = lane % 8;
+                        const u32x4 d = *(const u32x4 *)(epi_lds + r * C::EPI_RS + cc * 16);
+                        const int m = wm * C::WM + i * 16 + r;
+                        __builtin_amdgcn_raw_buffer_store_b128(d, qr, (int)((int64_t)m * N + wn * C::WN + cc * 16), 0,
+                                                               0);
+                    }
+                    const int64_t NB = N / 128;
+                    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ys + g.row_begin * NB, rows * NB * 4);
+                    if (fg == 0)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __builtin_bit_cast(uint32_t, bq.s), sr,
+                            (int)(((int64_t)(wm * C::WM + i * 16 + fr) * NB + g.n0 / 128 + wn) * 4), 0, 0);
+                }
+                if (want_y) {
 #pragma unroll
                 for (int c = 0; c < C::WN / C::EPI_CW; ++c) {
 #pragma unroll
-                    for (int jj = 0; jj < C::EPI_CW / 16; ++jj) {
-                        const int j = c * (C::EPI_CW / 16) + jj;
-                        const v4f v = acc[i][j];
-                        const bf2 p0 = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1), bf2);
-                        const bf2 p1 = __builtin_convertvector(__builtin_shufflevector(v, v, 2, 3), bf2);
-                        *(u32x2 *)(epi_lds + fr * C::EPI_RS + jj * 32 + fg * 8) =
-                            u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-                        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-                    }
+                    for (int jj = 0; jj < C::EPI_CW / 16; ++jj)
+                        *(u32x2 *)(epi_lds + fr * C::EPI_RS + jj * 32 + fg * 8) = bw_of(c * (C::EPI_CW / 16) + jj);
 #pragma unroll
                     for (int h = 0; h < 16 / RPI; ++h) {
                         const int r = h * RPI + lane / LPR, cc = lane % LPR;
@@ -956,6 +1017,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                         __builtin_amdgcn_raw_buffer_store_b128(d, yr, (int)(((int64_t)m * N + n) * 2), 0, 0);
                     }
                 }
+                }
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
             }
             return;
         }
@@ -1647,6 +1712,65 @@ hipError_t launch_linear(const void *x, const void *wq, const float *ws, int64_t
     if (e != hipSuccess)
         return e;
     return launch_gemm(xq, xs, wq, ws, M, N, K, y, out_fp32, pow2, gws, stream);
+}
+
+// ---- the GEMM whose epilogue quantizes its output (next layer's FP8 input) ----
+//
+// Fused where the dense plan is the unsplit 256 x 256 persistent kernel (each
+// wave then holds whole 128-column blocks of its rows); elsewhere the GEMM
+// writes bf16 Y (the caller's, or the workspace's when the caller wants none)
+// and the activation quantizer reads it back.
+static bool gemm_quant_fused(int64_t M, int64_t N, int64_t K)
+{
+    const Plan p = plan_dense(M, N, K);
+    return p.kind == K_DMA256 && p.ksplit == 1;
+}
+
+size_t gemm_quant_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || gemm_quant_fused(M, N, K))
+        return 0;
+    return align16((size_t)M * (size_t)N * 2) + gemm_workspace_size(M, N, K);
+}
+
+hipError_t launch_gemm_quant(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                             int64_t K, void *y, void *yq, float *ys, int mode, void *workspace, hipStream_t stream)
+{
+    if (M == 0)
+        return hipSuccess;
+    const bool pow2 = mode == SCALE_POW2;
+    if (gemm_quant_fused(M, N, K)) {
+        GemmArgs a = {};
+        a.xq = (const uint8_t *)xq;
+        a.xs = xs;
+        a.wq = (const uint8_t *)wq;
+        a.ws = ws;
+        a.y = y;
+        a.yq = (uint8_t *)yq;
+        a.ys = ys;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        const Plan p = plan_dense(M, N, K);
+        a.tiles_m = p.tiles_m;
+        a.tiles_n = p.tiles_n;
+        a.ksplit = 1;
+        const int units = a.tiles_m * a.tiles_n;
+        const int grid = units < kPersistentGrid ? units : kPersistentGrid;
+        if (pow2)
+            return launch(gemm_dma_kernel<256, 256, 4, 2, false, false, false, true, false, 2>, dim3(grid),
+                          dim3(512), 0, stream, a);
+        return launch(gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, false, 1>, dim3(grid), dim3(512),
+                      0, stream, a);
+    }
+    void *yb = y != nullptr ? y : workspace;
+    void *gws = (uint8_t *)workspace + align16((size_t)M * (size_t)N * 2);
+    // the kernel fp8_block_gemm itself would run (one row: the GEMV), so that Y is its Y
+    const hipError_t e = gemv_ok(M, N, K) ? launch_gemv(xq, xs, wq, ws, N, K, yb, 0, 0, stream)
+                                          : launch_gemm(xq, xs, wq, ws, M, N, K, yb, 0, pow2 ? 1 : 0, gws, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch_quant_act(yb, M, N, yq, ys, mode, stream);
 }
 
 // Grouped workspace: the two tile counts, padded to 16 bytes, then table A

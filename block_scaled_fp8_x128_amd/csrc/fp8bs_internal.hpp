@@ -77,6 +77,12 @@ hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, co
 size_t linear_workspace_size(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(const void *x, const void *wq, const float *ws, int64_t M, int64_t N, int64_t K, void *y,
                          int out_fp32, int pow2, void *workspace, hipStream_t stream);
+// Y = fp8_block_gemm(...) (bf16, written to y unless y is null) together with
+// quant_act_1x128(Y) into yq [M, N], ys [M, N/128]; mode is the scale mode of
+// the operands and of the output's quantization.
+size_t gemm_quant_workspace_size(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_quant(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                             int64_t K, void *y, void *yq, float *ys, int mode, void *workspace, hipStream_t stream);
 // One activation row on the vector ALUs (fp8bs_gemv.hip): gemv_ok says
 // whether the product qualifies (M == 1, K <= 16384); quantize 0 takes codes
 // and scales, 1 / 2 bf16 activations quantized in-kernel (EXACT / POW2), with

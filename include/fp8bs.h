@@ -349,6 +349,33 @@ FP8BS_API int fp8_block_grouped_gemm_pow2(const void *xq, const float *xs, const
                                           size_t workspace_bytes, void *stream);
 
 /*
+ * fp8_block_gemm_quant -- the block-scaled GEMM whose output is also the next
+ * FP8 layer's input: Y = fp8_block_gemm(xq, xs, wq, ws) in bf16, together with
+ * quant_act_1x128(Y), computed in the GEMM's epilogue where the shape allows
+ * (article section "Real-world performance gains": quantization kernels are
+ * one of the two costs that keep the linear-layer gain below the FP8 peak's
+ * 2x; quantizing in the producing kernel removes the separate pass over Y).
+ *   xq, xs, wq, ws, M, N, K: as fp8_block_gemm (K and N multiples of 128).
+ *   scale_mode: FP8BS_SCALE_EXACT or FP8BS_SCALE_POW2 -- the scales of the
+ *     operands (POW2: as fp8_block_gemm_pow2, with its precondition) and of
+ *     the output's quantization.
+ *   y: bf16 [M, N] (round to nearest even of the fp32 accumulator), or NULL
+ *     when only the quantized output is wanted.
+ *   yq [M, N] codes and ys [M, N/128] fp32 scales: bit for bit what
+ *     quant_act_1x128(Y, scale_mode) writes for this call's bf16 Y.
+ * Workspace: fp8bs_gemm_quant_workspace_size(M, N, K) bytes, 0 where the
+ *   quantization runs in the GEMM's epilogue (the large products: each
+ *   256 x 256 output tile's waves hold whole 128-column blocks of their rows);
+ *   elsewhere a bf16 Y buffer (used when y is NULL) followed by
+ *   fp8_block_gemm's own workspace, and the quantizer runs as a second launch.
+ * Errors: as fp8_block_gemm; y may be NULL, yq and ys may not (unless M == 0).
+ */
+FP8BS_API size_t fp8bs_gemm_quant_workspace_size(int64_t M, int64_t N, int64_t K);
+FP8BS_API int fp8_block_gemm_quant(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M,
+                                   int64_t N, int64_t K, void *y, void *yq, float *ys, int scale_mode,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * fp8_block_grouped_gemm_noalloc -- fp8_block_grouped_gemm for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  It takes no workspace and calls no

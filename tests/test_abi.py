@@ -212,6 +212,33 @@ def test_gemm_validation(fp8bs):
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 256, FAKE, 0, NULL, 0, NULL) == 4   # no table space
 
 
+def test_gemm_quant_workspace_and_validation(fp8bs):
+    """fp8_block_gemm_quant: no workspace where the quantization runs in the 256x256 kernel's
+    epilogue (at least one 256x256 tile per compute unit); elsewhere a bf16 Y buffer (16-byte
+    aligned) followed by fp8_block_gemm's workspace.  y may be NULL; yq and ys may not."""
+    L = fp8bs.lib()
+    wsz = L.fp8bs_gemm_quant_workspace_size
+    for M, N, K in ((8192, 4096, 4096), (8192, 28672, 4096), (8200, 8192, 1024)):
+        assert wsz(M, N, K) == 0
+    for M, N, K in ((300, 512, 1024), (1, 256, 2048), (64, 4096, 14336)):
+        assert wsz(M, N, K) == (M * N * 2 + 15) // 16 * 16 + L.fp8bs_gemm_workspace_size(M, N, K)
+    assert wsz(0, 128, 128) == 0
+    g = L.fp8_block_gemm_quant
+    F = FAKE
+    assert g(F, F, F, F, 8, 128, 128, F, F, F, 2, NULL, 0, NULL) == 1        # scale mode
+    assert g(F, F, F, F, 8, 100, 128, F, F, F, 0, NULL, 0, NULL) == 2        # N % 128
+    assert g(F, F, F, F, -8, 128, 128, F, F, F, 0, NULL, 0, NULL) == 1       # M < 0
+    assert g(F, F, F, F, 8, 128, 128, F, NULL, F, 0, NULL, 0, NULL) == 1     # null codes out
+    assert g(F, F, F, F, 8, 128, 128, F, F, NULL, 0, NULL, 0, NULL) == 1     # null scales out
+    assert g(F, F, F, F, 8, 128, 128, MISAL, F, F, 0, NULL, 0, NULL) == 1    # misaligned y
+    assert g(F, F, F, F, 8, 128, 128, F, MISAL, F, 0, NULL, 0, NULL) == 1    # misaligned codes
+    assert g(NULL, NULL, F, F, 0, 128, 128, NULL, NULL, NULL, 1, NULL, 0, NULL) == 0   # M == 0
+    need = wsz(300, 512, 1024)
+    assert g(F, F, F, F, 300, 512, 1024, NULL, F, F, 0, NULL, 0, NULL) == 4            # no workspace
+    assert g(F, F, F, F, 300, 512, 1024, NULL, F, F, 0, F, need - 1, NULL) == 4       # too small
+    assert g(F, F, F, F, 300, 512, 1024, NULL, F, F, 0, MISAL, need, NULL) == 1       # misaligned
+
+
 def test_grouped_noalloc_validation(fp8bs):
     """fp8_block_grouped_gemm_noalloc: the grouped GEMM's checks, no workspace argument, and
     SCRATCH_TOO_SMALL (before any device call) when its row-tile tables exceed the library's
