@@ -50,6 +50,8 @@ EXPORTS = (
     "fp8_block_grouped_gemm_pow2",
     "fp8_block_gemm_quant",
     "fp8bs_gemm_quant_workspace_size",
+    "fp8_kv_attention_decode",
+    "fp8bs_kv_attention_workspace_size",
     "fp8_block_grouped_gemm_noalloc",
     "fp8_block_linear",
     "fp8_block_linear_pow2",
@@ -95,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.fp8_block_gemm_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P, I32, P, SZ, P]
         L.fp8bs_gemm_quant_workspace_size.argtypes = [I64, I64, I64]
         L.fp8bs_gemm_quant_workspace_size.restype = SZ
+        L.fp8_kv_attention_decode.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, I32, P, SZ, P]
+        L.fp8bs_kv_attention_workspace_size.argtypes = [I64, I64, I64, I64]
+        L.fp8bs_kv_attention_workspace_size.restype = SZ
         L.fp8_block_linear.argtypes = [P, P, P, I64, I64, I64, P, I32, P, SZ, P]
         L.fp8_block_linear_pow2.argtypes = L.fp8_block_linear.argtypes
         L.fp8bs_linear_workspace_size.argtypes = [I64, I64, I64]
@@ -111,7 +116,7 @@ def lib() -> ctypes.CDLL:
                    "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
-                   "fp8_block_grouped_gemm_noalloc", "fp8_block_gemm_quant",
+                   "fp8_block_grouped_gemm_noalloc", "fp8_block_gemm_quant", "fp8_kv_attention_decode",
                    "fp8_block_linear", "fp8_block_linear_pow2"):
             getattr(L, fn).restype = I32
         _lib = L
@@ -556,3 +561,37 @@ def _grouped(fn, xq, xs, wq, ws, group_offsets, out_dtype, out, workspace, noall
     _check(fn, st)
     return out
 
+
+# ---- attention over an FP8 KV cache ---------------------------------------------
+
+def kv_attention_workspace_size(B: int, T: int, Hq: int, Hkv: int) -> int:
+    return int(lib().fp8bs_kv_attention_workspace_size(B, T, Hq, Hkv))
+
+
+def fp8_kv_attention_decode(q, kq, ks, vq, vs, lens, sm_scale: float, out_dtype=torch.bfloat16, out=None,
+                            workspace=None):
+    """o [B, Hq, 128]: each sequence's new query token q [B, Hq, 128] (bf16) attending to
+    its first lens[b] cached tokens; kq, vq [B, T, Hkv, 128] codes and ks, vs [B, T, Hkv]
+    scales (quant_act_1x128 of the key / value rows); lens int32 [B] on the device."""
+    q = _bf16_payload(q, "q")
+    kq, vq = _codes(kq, "kq"), _codes(vq, "vq")
+    ks, vs = _f32(ks, "ks"), _f32(vs, "vs")
+    if q.dim() != 3 or kq.dim() != 4 or q.shape[2] != 128 or kq.shape[3] != 128:
+        raise ValueError("q must be [B, Hq, 128] and kq [B, T, Hkv, 128]")
+    B, Hq, _ = q.shape
+    _, T, Hkv, _ = kq.shape
+    if kq.shape[0] != B or vq.shape != kq.shape or ks.shape != (B, T, Hkv) or vs.shape != ks.shape:
+        raise ValueError("cache shapes do not match")
+    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 [B] tensor")
+    _same_device(q.device, ("kq", kq), ("ks", ks), ("vq", vq), ("vs", vs), ("lens", lens))
+    code = _out_code(out_dtype)
+    dt = torch.bfloat16 if code == OUT_BF16 else torch.float32
+    out = torch.empty((B, Hq, 128), dtype=dt, device=q.device) if out is None else \
+        _out(out, (B, Hq, 128), (dt,), q.device, "out")
+    workspace = _workspace(workspace, kv_attention_workspace_size(B, T, Hq, Hkv), q.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fp8_kv_attention_decode(_ptr(q), _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _ptr(lens), B, T, Hq, Hkv,
+                                       float(sm_scale), _ptr(out), code, _ptr(workspace), wsz, _stream(q))
+    _check("fp8_kv_attention_decode", st)
+    return out

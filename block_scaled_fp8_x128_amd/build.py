@@ -31,7 +31,8 @@ FLAGS = [
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC,
 ]
 
-SOURCES = ["fp8bs_abi.hip", "fp8bs_quant.hip", "fp8bs_gemm.hip", "fp8bs_gemv.hip", "fp8bs_swiglu.hip", "fp8bs_route.hip"]
+SOURCES = ["fp8bs_abi.hip", "fp8bs_quant.hip", "fp8bs_gemm.hip", "fp8bs_gemv.hip", "fp8bs_swiglu.hip", "fp8bs_route.hip",
+           "fp8bs_attn.hip"]
 
 
 def _compile(src: str) -> str:

@@ -525,4 +525,42 @@ int fp8_block_gemm_quant(const void *xq, const float *xs, const void *wq, const 
                                               (hipStream_t)stream));
 }
 
+size_t fp8bs_kv_attention_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv)
+{
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || !fp8bs::kv_attention_group_ok(Hq, Hkv))
+        return 0;
+    return fp8bs::kv_attention_workspace_size(B, T, Hq, Hkv);
+}
+
+int fp8_kv_attention_decode(const void *q_bf16, const void *kq, const float *ks, const void *vq, const float *vs,
+                            const int32_t *lens, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, float sm_scale,
+                            void *out, int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || !(sm_scale == sm_scale) || sm_scale > 3.0e38f ||
+        sm_scale < -3.0e38f || (out_dtype != FP8BS_OUT_BF16 && out_dtype != FP8BS_OUT_FP32))
+        return FP8BS_INVALID_ARG;
+    if (!fp8bs::kv_attention_group_ok(Hq, Hkv))
+        return FP8BS_UNSUPPORTED_SHAPE;
+    // 32-bit byte offsets within one sequence's cache rows; workgroup counts
+    if (T * Hkv * 128 >= kMaxDim || B * Hkv >= kMaxDim || B * Hq >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (B == 0)
+        return FP8BS_OK;
+    const int64_t cache = B * T * Hkv * 128;
+    if (!tensor_ok(q_bf16, B * Hq * 128, 16) || !tensor_ok(kq, cache, 16) || !tensor_ok(vq, cache, 16) ||
+        !tensor_ok(ks, cache, 4) || !tensor_ok(vs, cache, 4) || !tensor_ok(lens, B, 4) ||
+        !tensor_ok(out, B * Hq * 128, 16))
+        return FP8BS_INVALID_ARG;
+    const size_t need = fp8bs::kv_attention_workspace_size(B, T, Hq, Hkv);
+    if (workspace_bytes < need)
+        return FP8BS_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16)))
+        return FP8BS_INVALID_ARG;
+    int st = check_device();
+    if (st != FP8BS_OK)
+        return st;
+    return status_of(fp8bs::launch_kv_attention(q_bf16, kq, ks, vq, vs, lens, B, T, Hq, Hkv, sm_scale, out,
+                                                out_dtype == FP8BS_OUT_FP32, workspace, (hipStream_t)stream));
+}
+
 } // extern "C"

@@ -100,4 +100,13 @@ hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, 
 constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
 hipError_t noalloc_scratch(void **ptr);
 
+// ---- attention over an FP8 KV cache (fp8bs_attn.hip) -------------------------
+
+// Hq / Hkv in {1, 2, 4, 8}
+bool kv_attention_group_ok(int64_t Hq, int64_t Hkv);
+size_t kv_attention_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv);
+hipError_t launch_kv_attention(const void *q, const void *kq, const float *ks, const void *vq, const float *vs,
+                               const int32_t *lens, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, float sm_scale,
+                               void *out, int out_fp32, void *workspace, hipStream_t stream);
+
 } // namespace fp8bs

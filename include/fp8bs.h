@@ -376,6 +376,37 @@ FP8BS_API int fp8_block_gemm_quant(const void *xq, const float *xs, const void *
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fp8_kv_attention_decode -- attention of one new query token per sequence
+ * over an FP8 KV cache (rollout decode; article section "Real-world
+ * performance gains": an FP8 KV cache and FP8 attention lift the end-to-end
+ * gain to about 48%).
+ *   q [B, Hq, 128] bf16: the query heads of each sequence's new token.
+ *   kq, vq [B, T, Hkv, 128] E4M3 codes and ks, vs [B, T, Hkv] fp32 scales:
+ *     keys and values cached with one scale per (token, head) -- exactly
+ *     quant_act_1x128 of the [B * T, Hkv * 128] key and value rows, so a
+ *     cache is filled (or a token appended at row b * T + t) by that call.
+ *   lens: DEVICE int32 [B]; sequence b attends to its cached tokens
+ *     0 .. lens[b] - 1 (clamped to [0, T]; an empty context gives 0).
+ *   Query head h reads key/value head h / (Hq / Hkv); Hq / Hkv must be 1, 2,
+ *     4 or 8 (grouped queries).  The head dimension is 128.
+ *   o[b, h, :] = sum_j softmax_j(sm_scale * ks * q . decode(k_j)) * vs * decode(v_j),
+ *     written to out [B, Hq, 128] as bf16 (round to nearest even of the fp32
+ *     result) or fp32 (out_dtype).  Scores use the matrix cores on bf16 (key
+ *     codes decode exactly; products are exact), the rest is fp32.
+ * Workspace: fp8bs_kv_attention_workspace_size(B, T, Hq, Hkv) bytes (the
+ *   per-split partial states when a sequence's tokens are split over several
+ *   workgroups; 0 otherwise).  It need not be zeroed.
+ * Errors: INVALID_ARG for null/misaligned pointers, negative sizes, a
+ *   non-finite sm_scale or an unknown out_dtype; UNSUPPORTED_SHAPE for other
+ *   group sizes or T * Hkv * 128 >= 2^31; WORKSPACE_TOO_SMALL.
+ */
+FP8BS_API size_t fp8bs_kv_attention_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv);
+FP8BS_API int fp8_kv_attention_decode(const void *q_bf16, const void *kq, const float *ks, const void *vq,
+                                      const float *vs, const int32_t *lens, int64_t B, int64_t T, int64_t Hq,
+                                      int64_t Hkv, float sm_scale, void *out, int out_dtype, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
  * fp8_block_grouped_gemm_noalloc -- fp8_block_grouped_gemm for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  It takes no workspace and calls no

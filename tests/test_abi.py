@@ -239,6 +239,35 @@ def test_gemm_quant_workspace_and_validation(fp8bs):
     assert g(F, F, F, F, 300, 512, 1024, NULL, F, F, 0, MISAL, need, NULL) == 1       # misaligned
 
 
+def test_kv_attention_workspace_and_validation(fp8bs):
+    """fp8_kv_attention_decode: group sizes 1, 2, 4, 8; per-split partial states (2 + 128 fp32 per
+    sequence, query head and split) when a sequence's tokens are split; argument checks."""
+    L = fp8bs.lib()
+    wsz = L.fp8bs_kv_attention_workspace_size
+    assert wsz(4, 1024, 32, 8) % (4 * 32 * 130 * 4) == 0
+    assert wsz(64, 4096, 32, 8) == 0 or wsz(64, 4096, 32, 8) % (64 * 32 * 130 * 4) == 0
+    assert wsz(8, 4096, 32, 8) > 0            # 64 key/value heads: split to fill the chip
+    assert wsz(1, 64, 32, 8) == 0             # one 64-token chunk: not split
+    assert wsz(2, 100, 12, 8) == 0            # unsupported group: no workspace
+    f = L.fp8_kv_attention_decode
+    F = FAKE
+    args = lambda B, T, Hq, Hkv, sm=0.1, od=0: (F, F, F, F, F, F, B, T, Hq, Hkv, ctypes.c_float(sm), F, od,  # noqa
+                                                F, 1 << 30, NULL)
+    assert f(*args(2, 100, 12, 8)) == 2                  # Hq / Hkv not an integer
+    assert f(*args(2, 100, 48, 4)) == 2                  # group of 12
+    assert f(*args(2, 100, 32, 2)) == 2                  # group of 16
+    assert f(*args(-1, 100, 32, 8)) == 1                 # B < 0
+    assert f(*args(2, 0, 32, 8)) == 1                    # T == 0
+    assert f(*args(2, 100, 32, 8, od=4)) == 1            # out dtype
+    assert f(*args(2, 100, 32, 8, sm=float("nan"))) == 1  # sm_scale
+    assert f(*args(2, 1 << 22, 32, 8)) == 2              # 32-bit cache offsets
+    assert f(*args(0, 100, 32, 8)) == 0                  # B == 0: no-op
+    assert f(F, F, F, F, F, NULL, 2, 100, 32, 8, ctypes.c_float(0.1), F, 0, F, 1 << 30, NULL) == 1  # lens
+    assert f(F, F, F, F, F, F, 2, 100, 32, 8, ctypes.c_float(0.1), MISAL, 0, F, 1 << 30, NULL) == 1  # out
+    need = wsz(8, 4096, 32, 8)
+    assert f(F, F, F, F, F, F, 8, 4096, 32, 8, ctypes.c_float(0.1), F, 0, F, need - 1, NULL) == 4
+
+
 def test_grouped_noalloc_validation(fp8bs):
     """fp8_block_grouped_gemm_noalloc: the grouped GEMM's checks, no workspace argument, and
     SCRATCH_TOO_SMALL (before any device call) when its row-tile tables exceed the library's
