@@ -49,8 +49,11 @@ __global__ __launch_bounds__(RG_THREADS) void quant_act_gather_kernel(const uint
         if (b < nblocks) {
             const uint32_t m = b / KB, kb = b - m * KB;
             const int64_t r = rows[m];
+            // an ordinary (cached) load: each token row is read once per expert it
+            // is routed to, and the token tensor fits the caches, so its repeats
+            // hit there (a nontemporal load sent every repeat to HBM)
             if (r >= 0 && r < T)
-                v[j] = __builtin_nontemporal_load((const u32x4 *)(x + r * K + (int64_t)kb * 128) + c);
+                v[j] = *((const u32x4 *)(x + r * K + (int64_t)kb * 128) + c);
         }
     }
 #pragma unroll
