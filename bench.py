@@ -2,7 +2,16 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input.
 Workloads (--workload):
-  dense  (default) 8B-shaped dense layer at M = 8192 tokens: per-step
+  all    (default) the dense layer below in EXACT mode is the headline (value,
+         roofline, cpu_baseline); then every other measured row, each with its
+         own roofline object and oracle CPU baseline (all threads and one):
+         d1 the 32-layer recalibration (EXACT, POW2), d2 the activation
+         quantizer alone at its four shapes beside a device copy of the same
+         bytes, d3 the dense layer with power-of-2 scales, d4 the decode grid,
+         d5 the MoE layer (EXACT, POW2), d6 the tiny layer's latency, the
+         GEMM that quantizes its own output against GEMM + quantizer, and
+         the decode attention over an FP8 KV cache.
+  dense  8B-shaped dense layer at M = 8192 tokens: per-step
          recalibration of the layer's four weights (128x128 quantizer), the
          1x128 quantization of each GEMM input, and the four block-scaled
          GEMMs QKV (K 4096, N 6144), gate+up (K 4096, N 28672),
@@ -162,10 +171,7 @@ def traffic_for(workload):
 # workloads
 # ---------------------------------------------------------------------------
 
-def dense_workload(fp8bs, dev, mode):
-    # POW2 scales go to the entry points that apply them through the matrix cores
-    gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
-    grouped = fp8bs.fp8_block_grouped_gemm_pow2 if mode else fp8bs.fp8_block_grouped_gemm
+def dense_data(dev):
     import synth
     import torch
     M = 8192
@@ -180,7 +186,12 @@ def dense_workload(fp8bs, dev, mode):
         ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         bufs.append(dict(name=name, M=M, N=N, K=K, x=x, w=w, xq=xq, xs=xs, wq=wq, ws=ws, y=y))
+    return bufs
 
+
+def dense_step(fp8bs, bufs, mode):
+    # POW2 scales go to the entry points that apply them through the matrix cores
+    gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
     w_all = [b["w"] for b in bufs]
     out_all = [(b["wq"], b["ws"]) for b in bufs]
 
@@ -192,8 +203,13 @@ def dense_workload(fp8bs, dev, mode):
             maybe(timer, "gemm_" + b["name"],
                   lambda: gemm(b["xq"], b["xs"], b["wq"], b["ws"], out=b["y"]))
 
+    return step
+
+
+def dense_workload(fp8bs, dev, mode):
+    bufs = dense_data(dev)
     flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
-    return step, bufs, flops
+    return dense_step(fp8bs, bufs, mode), bufs, flops
 
 
 def train_workload(fp8bs, dev, mode):
@@ -386,10 +402,10 @@ def decode_workload(fp8bs, dev, mode):
         # infinity cache never holds the weights a GEMM reads
         copies = []
         for c in range(5):
-            wq, ws = fp8bs.quant_w_128x128(bf16_dev(synth.weights(N, K, sub=synth.sub_layer(40 + c)), dev), mode)
+            wq, ws = fp8bs.quant_w_128x128(synth.weights_dev(N, K, dev, sub=synth.sub_layer(40 + c)), mode)
             copies.append((wq, ws))
         for j, M in enumerate((1, 16, 64, 256)):
-            x = bf16_dev(synth.activations(M, K, sub=synth.SUB_X + M), dev)
+            x = synth.activations_dev(M, K, dev, sub=synth.SUB_X + M)
             pairs.append(dict(name="%s_m%d" % (wname, M), M=M, N=N, K=K, x=x, copies=copies, j=j,
                               xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
                               xs=torch.empty((M, K // 128), dtype=torch.float32, device=dev),
@@ -440,12 +456,11 @@ def moe_workload(fp8bs, dev, mode):
     row_token, offs = synth.moe_routing(T, E, TOPK)
     Mt = int(offs[-1])
     log("MoE: %d routed rows, per-expert rows min %d max %d" % (Mt, int(np.diff(offs).min()), int(np.diff(offs).max())))
-    x_tok = synth.activations(T, H, sub=synth.SUB_X)
     # the dispatch: each routed row reads its token's row (quantized on the way, in expert order)
-    xt = bf16_dev(x_tok, dev)
+    xt = synth.activations_dev(T, H, dev, sub=synth.SUB_X)
     rows_d = torch.from_numpy(np.ascontiguousarray(row_token, dtype=np.int32)).to(dev)
-    w1 = bf16_dev(synth.expert_weights(E, 2 * F, H, sub=synth.SUB_W).reshape(E * 2 * F, H), dev)
-    w2 = bf16_dev(synth.expert_weights(E, H, F, sub=synth.SUB_W + 1).reshape(E * H, F), dev)
+    w1 = synth.weights_dev(E * 2 * F, H, dev, sub=synth.SUB_W)
+    w2 = synth.weights_dev(E * H, F, dev, sub=synth.SUB_W + 1)
     offs_d = torch.from_numpy(offs).to(dev)
     b = dict(
         x1q=torch.empty((Mt, H), dtype=torch.uint8, device=dev), x1s=torch.empty((Mt, H // 128), dtype=torch.float32,
@@ -479,6 +494,477 @@ def moe_workload(fp8bs, dev, mode):
     shapes = {"gate_up": (Mt, 2 * F, H), "down": (Mt, H, F)}
     flops = sum(2.0 * m * n * k for m, n, k in shapes.values())
     return step, shapes, flops, E
+
+
+# ---------------------------------------------------------------------------
+# the default run: every measured row of the hot path
+# ---------------------------------------------------------------------------
+
+CPU_TARGET_S = 2.5  # wall time per oracle sample and thread count (all threads, then one)
+ACT_BPE = 3.0 + 4.0 / 128      # activation quantizer: bf16 in, code out, one fp32 per 128
+W_BPE = 3.0 + 4.0 / 16384      # weight quantizer: the same with one fp32 per 128 x 128
+
+
+def cpu_row(make, work_of, unit, describe, n0, nmax, target_s=CPU_TARGET_S):
+    """The oracle on a bounded sample: make(n) prepares a sample of size n
+    (outside the clock) and returns (callable, n actually used); the sample
+    grows until one call takes target_s, once with all of the oracle's threads
+    and once with one.  value = work_of(n) / seconds."""
+    import oracle
+    allt = oracle.max_threads()
+    res = {}
+    for th in (allt, 1):
+        oracle.set_threads(th)
+        n = n0
+        while True:
+            f, n_used = make(n)
+            t0 = time.perf_counter()
+            f()
+            dt = time.perf_counter() - t0
+            if dt >= target_s or n_used >= nmax:
+                break
+            n = min(nmax, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
+        res[th] = (n_used, dt)
+    oracle.set_threads(allt)
+    (n, dt), (n1, dt1) = res[allt], res[1]
+    return {"value": work_of(n) / dt, "unit": unit, "cores": allt, "kind": "oracle",
+            "sample": describe(n, dt), "value_1thread": work_of(n1) / dt1, "sample_1thread": describe(n1, dt1)}
+
+
+def roof_hbm(kernel, ms, nbytes, traffic=None, tsrc=None):
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": tsrc,
+            "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 4)}
+
+
+def roof_mfma(kernel, ms, flops, traffic=None, tsrc=None):
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "traffic_source": tsrc,
+            "algorithmic_flop_per_launch": flops, "avg_launch_ms": round(ms, 4)}
+
+
+def roof_binding(kernel, ms, flops, nbytes, traffic=None, tsrc=None):
+    """The roofline that binds: HBM when the algorithmic bytes at the HBM peak take
+    longer than the FLOPs at the FP8 peak, else the matrix cores."""
+    if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_FP8_TFLOPS * 1e12):
+        r = roof_hbm(kernel, ms, nbytes, traffic, tsrc)
+        r["algorithmic_flop_per_launch"] = flops
+    else:
+        r = roof_mfma(kernel, ms, flops, traffic, tsrc)
+        r["algorithmic_bytes_per_launch"] = nbytes
+    return r
+
+
+def with_spread(kernels, timer):
+    for k, v in kernels.items():
+        if isinstance(v, dict) and k in timer.pairs:
+            med, mn = timer.spread(k)
+            v["median_ms"], v["min_ms"] = round(med, 4), round(mn, 4)
+    return kernels
+
+
+def cpu_recal(target_s=CPU_TARGET_S):
+    """d1: the oracle's 128x128 quantizer on the first rows of a 28672 x 4096 weight."""
+    import oracle
+    import synth
+    w = synth.weights(28672, 4096, sub=synth.sub_layer(0))
+
+    def make(n):
+        r = max(128, min(28672, n // (128 * 4096) * 128))
+        wr = np.ascontiguousarray(w[:r])
+        return (lambda: oracle.quant_w_128x128(wr, 0)), r * 4096
+    return cpu_row(make, lambda n: n * W_BPE / 1e9, "GB/s",
+                   lambda n, dt: "quant_w_128x128 (EXACT) of the first %d rows of one 28672 x 4096 weight, %.2f s "
+                                 "wall" % (n // 4096, dt), 1 << 21, 28672 * 4096, target_s)
+
+
+def cpu_quant_act(target_s=CPU_TARGET_S):
+    """d2: the oracle's 1x128 quantizer on the first rows of X [8192, 4096]."""
+    import oracle
+    import synth
+    x = synth.activations(8192, 4096, sub=synth.SUB_X)
+
+    def make(n):
+        r = max(1, min(8192, n // 4096))
+        xr = np.ascontiguousarray(x[:r])
+        return (lambda: oracle.quant_act_1x128(xr, 0)), r * 4096
+    return cpu_row(make, lambda n: n * ACT_BPE / 1e9, "GB/s",
+                   lambda n, dt: "quant_act_1x128 (EXACT) of the first %d rows of X [8192, 4096], %.2f s wall"
+                                 % (n // 4096, dt), 1 << 20, 8192 * 4096, target_s)
+
+
+def cpu_decode(target_s=CPU_TARGET_S):
+    """d4: the oracle's linear layer (quant_act_1x128 + gemm_full) at M = 16 against the gate+up weight."""
+    import oracle
+    import synth
+    N, K = 28672, 4096
+    w = synth.weights(N, K, sub=synth.sub_layer(40))
+    wq, ws = oracle.quant_w_128x128(w)
+    x = synth.activations(16, K, sub=synth.SUB_X + 16)
+
+    def make(n):
+        reps = max(1, n)
+
+        def f():
+            for _ in range(reps):
+                xq, xs = oracle.quant_act_1x128(x)
+                oracle.gemm_full(xq, xs, wq, ws)
+        return f, reps
+    lb = N * K * (1 + 4 / 16384) + 16 * N * 2 + 16 * K * 2
+    return cpu_row(make, lambda r: r * lb / 1e9, "GB/s",
+                   lambda r, dt: "%d oracle linear layers (quant_act_1x128 + gemm_full) at M = 16 against the "
+                                 "gate+up weight, %.2f s wall" % (r, dt), 1, 64, target_s)
+
+
+def cpu_moe(target_s=CPU_TARGET_S, experts=16):
+    """d5: the oracle's full-output grouped GEMM (gate+up) over the first experts' routed rows."""
+    import oracle
+    import synth
+    row_token, offs = synth.moe_routing(T_TOKENS, 128, 8)
+    N, K = 1536, 2048
+    x_tok = synth.activations(T_TOKENS, K, sub=synth.SUB_X)
+    w = synth.weights(experts * N, K, sub=synth.SUB_W)
+    wq, ws = oracle.quant_w_128x128(w)
+    wq, ws = wq.reshape(experts, N, K), ws.reshape(experts, N // 128, K // 128)
+
+    def make(n):
+        e = max(1, min(experts, n))
+        xq, xs = oracle.quant_act_1x128(np.ascontiguousarray(x_tok[row_token[:int(offs[e])]]))
+        return (lambda: oracle.grouped_gemm_full(xq, xs, wq[:e], ws[:e], offs[:e + 1])), e
+    return cpu_row(make, lambda e: 2.0 * int(offs[e]) * N * K / 1e12, "TFLOP/s",
+                   lambda e, dt: "grouped_gemm_full (every output) of the gate+up GEMM over the first %d of 128 "
+                                 "experts (%d rows), %.2f s wall" % (e, int(offs[e]), dt), 1, experts, target_s)
+
+
+def cpu_tiny(target_s=CPU_TARGET_S):
+    """d6: the oracle's whole tiny layer (quant_act_1x128 + quant_w_128x128 + gemm_full), repeated."""
+    import oracle
+    import synth
+    xh, wh = synth.activations(256, 512), synth.weights(512, 512)
+
+    def make(n):
+        reps = max(1, n)
+
+        def f():
+            for _ in range(reps):
+                a, b = oracle.quant_act_1x128(xh)
+                c, d = oracle.quant_w_128x128(wh)
+                oracle.gemm_full(a, b, c, d)
+        return f, reps
+    cb = cpu_row(make, lambda r: r, "layers/s",
+                 lambda r, dt: "%d oracle tiny layers (quant_act_1x128 + quant_w_128x128 + gemm_full), %.2f s wall"
+                               % (r, dt), 1, 1 << 16, target_s)
+    cb["latency_ms"] = round(1e3 / cb["value"], 3)
+    cb["latency_ms_1thread"] = round(1e3 / cb["value_1thread"], 3)
+    return cb
+
+
+def row_recal(fp8bs, dev, steps, warmup, cpu):
+    """d1: 32 layers x 4 weights re-quantized, EXACT then POW2."""
+    timer = KernelTimer()
+    step, nbytes = recal_workload(fp8bs, dev)
+    ms = timed_loop(step, steps, warmup, timer)
+    traffic, tsrc = traffic_for("recal")
+    out = {"config": "32 layers x {6144x4096, 4096x4096, 28672x4096, 4096x14336} bf16 weights, 128x128 blocks, "
+                     "one quant_w_128x128_batched call per mode (32 tensors per launch)",
+           "ms_per_step": round(ms, 4), "bytes_per_pass": nbytes}
+    for mode, name in ((0, "exact"), (1, "pow2")):
+        t = timer.avg_ms("recal_" + name)
+        out[name] = {**hbm_entry(t, nbytes), "roofline": roof_hbm(DOMINANT["recal"][0].replace("<0>", "<%d>" % mode)
+                                                                  + " (batched)", t, nbytes,
+                                                                  *((traffic, tsrc) if mode == 0 else (None, None)))}
+    with_spread({"recal_exact": out["exact"], "recal_pow2": out["pow2"]}, timer)
+    if cpu:
+        out["cpu_baseline"] = cpu_recal()
+    return out
+
+
+def row_quant_act(fp8bs, dev, steps, warmup, cpu):
+    """d2: the activation quantizer alone at the four activation shapes, each
+    beside the runtime's device copy of the same byte count (half read, half
+    written); a 512 MiB write between launches keeps the inputs out of the
+    256 MB infinity cache."""
+    import synth
+    import torch
+    shapes = [(8192, 4096), (8192, 14336), (65536, 2048), (65536, 768)]
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {"config": "quant_act_1x128 (EXACT) alone on [8192,4096] and [8192,14336] (8B dense layer inputs) and "
+                     "[65536,2048] and [65536,768] (MoE gate+up and down inputs); cold inputs; "
+                     "copy = torch copy_ of a uint8 buffer of half the algorithmic bytes"}
+    timer = KernelTimer()
+    for i, (M, K) in enumerate(shapes):
+        x = synth.activations_dev(M, K, dev, sub=synth.SUB_X + 50 + i)
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+        nbytes = M * K * ACT_BPE
+        half = int(nbytes // 2) // 16 * 16
+        src = torch.empty(half, dtype=torch.uint8, device=dev)
+        dst = torch.empty(half, dtype=torch.uint8, device=dev)
+        name = "%dx%d" % (M, K)
+        for r in range(warmup + steps):
+            t = timer if r >= warmup else None
+            scrub.fill_(r & 0xFF)
+            maybe(t, "quant_" + name, lambda: fp8bs.quant_act_1x128(x, 0, out=(xq, xs)))
+            scrub.fill_((r + 1) & 0xFF)
+            maybe(t, "copy_" + name, lambda: dst.copy_(src))
+        torch.cuda.synchronize()
+        tq, tc = timer.avg_ms("quant_" + name), timer.avg_ms("copy_" + name)
+        med, mn = timer.spread("quant_" + name)
+        out[name] = {**hbm_entry(tq, nbytes), "median_ms": round(med, 4), "min_ms": round(mn, 4),
+                     "copy_ms": round(tc, 4), "copy_GB/s": round(2 * half / (tc * 1e-3) / 1e9, 1),
+                     "frac_of_copy": round(tc / tq, 4),
+                     "roofline": roof_hbm("fp8bs::quant_act_kernel", tq, nbytes)}
+        del x, xq, xs, src, dst
+    del scrub
+    torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = cpu_quant_act()
+    return out
+
+
+def row_dense_pow2(fp8bs, bufs, steps, warmup):
+    """d3 with power-of-2 scales: the same layer through the _pow2 entry points."""
+    timer = KernelTimer()
+    ms = timed_loop(dense_step(fp8bs, bufs, 1), steps, warmup, timer)
+    kernels, roof = summarize_dense(bufs, timer)
+    roof["kernel"] = roof["kernel"].replace("false, false, false, false, false>", "false, false, false, true, false>")
+    roof["traffic"], roof["traffic_source"] = None, None
+    flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
+    return {"ms_per_step": round(ms, 4), "TFLOP/s_step": round(flops / (ms * 1e-3) / 1e12, 2),
+            "roofline": roof, "kernels": with_spread(kernels, timer)}
+
+
+def cpu_dense(target_s=CPU_TARGET_S):
+    """d3: the oracle's full-output GEMM on the first rows of the gate+up GEMM."""
+    import oracle
+    import synth
+    N, K = 28672, 4096
+    w = synth.weights(N, K, sub=synth.sub_layer(1))
+    wq, ws = oracle.quant_w_128x128(w)
+    x = synth.activations(1024, K, sub=synth.SUB_X + 10)
+    xq, xs = oracle.quant_act_1x128(x)
+
+    def make(n):
+        r = max(1, min(1024, n))
+        a, b = np.ascontiguousarray(xq[:r]), np.ascontiguousarray(xs[:r])
+        return (lambda: oracle.gemm_full(a, b, wq, ws)), r
+    return cpu_row(make, lambda r: 2.0 * r * N * K / 1e12, "TFLOP/s",
+                   lambda r, dt: "gemm_full (every output) of the gate+up GEMM (N 28672, K 4096), first %d of 8192 "
+                                 "rows, %.2f s wall" % (r, dt), 8, 1024, target_s)
+
+
+def row_decode(fp8bs, dev, steps, warmup, cpu):
+    """d4: M in {1, 16, 64, 256} against the gate+up and down weights, through
+    fp8_block_linear, and the GEMM alone beside it; 5 rotated weight copies."""
+    timer = KernelTimer()
+    step, separate, pairs, flops = decode_workload(fp8bs, dev, 0)
+    ms = timed_loop(step, steps, warmup, timer)
+    separate(None, 2)
+    separate(timer, steps)
+    import torch
+    torch.cuda.synchronize()
+    out = {"config": "M in {1,16,64,256} x (gate+up K4096 N28672, down K14336 N4096), EXACT; linear = "
+                     "fp8_block_linear from bf16 X (one launch for M <= 16), gemm = fp8_block_gemm alone",
+           "ms_per_step": round(ms, 4)}
+    for p in pairs:
+        tl, tg = timer.avg_ms("linear_" + p["name"]), timer.avg_ms("gemm_" + p["name"])
+        wb = p["N"] * p["K"] * (1 + 4 / 16384) + p["M"] * p["N"] * 2
+        gbytes = wb + p["M"] * p["K"] * (1 + 4 / 128)
+        lbytes = wb + p["M"] * p["K"] * 2
+        fl = 2.0 * p["M"] * p["N"] * p["K"]
+        lm, lmin = timer.spread("linear_" + p["name"])
+        gm, gmin = timer.spread("gemm_" + p["name"])
+        out[p["name"]] = {
+            "linear": {**hbm_entry(tl, lbytes), "median_ms": round(lm, 4), "min_ms": round(lmin, 4),
+                       "fused": fp8bs.linear_workspace_size(p["M"], p["N"], p["K"]) == 0,
+                       "roofline": roof_hbm("fp8_block_linear", tl, lbytes)},
+            "gemm": {**hbm_entry(tg, gbytes), "median_ms": round(gm, 4), "min_ms": round(gmin, 4),
+                     "roofline": roof_binding("fp8_block_gemm", tg, fl, gbytes)}}
+    del pairs
+    torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = cpu_decode()
+    return out
+
+
+def row_moe(fp8bs, dev, steps, warmup, cpu):
+    """d5: the MoE layer, EXACT then POW2."""
+    import torch
+    out = {"config": "128 experts, hidden 2048, expert FFN 768, 8192 tokens top-8 (65536 rows): dispatch quantizer, "
+                     "grouped gate+up K2048 N1536, gated activation + quantizer, grouped down K768 N2048"}
+    for mode, mname in ((0, "exact"), (1, "pow2")):
+        timer = KernelTimer()
+        step, shapes, flops, E = moe_workload(fp8bs, dev, mode)
+        ms = timed_loop(step, steps, warmup, timer)
+        r = {"ms_per_step": round(ms, 4), "TFLOP/s_step": round(flops / (ms * 1e-3) / 1e12, 2)}
+        traffic, tsrc = traffic_for("moe") if mode == 0 else (None, None)
+        for name, (m, n, k) in shapes.items():
+            t = timer.avg_ms("grouped_" + name)
+            nbytes = m * k + m * k // 128 * 4 + E * n * k * (1 + 4 / 16384) + m * n * 2
+            fl = 2.0 * m * n * k
+            med, mn = timer.spread("grouped_" + name)
+            tr = (traffic, tsrc) if name == "gate_up" else (None, None)
+            r["grouped_" + name] = {"ms": round(t, 4), "median_ms": round(med, 4), "min_ms": round(mn, 4),
+                                    "roofline": roof_binding("fp8_block_grouped_gemm%s %s" %
+                                                             ("_pow2" if mode else "", name), t, fl, nbytes, *tr)}
+        m, _, k = shapes["gate_up"]
+        r["quant_act_gather_gate_up"] = hbm_entry(timer.avg_ms("quant_act_gather_gate_up"),
+                                                  T_TOKENS * k * 2 + m * 4 + m * k + m * k // 128 * 4)
+        m, _, k = shapes["down"]
+        r["swiglu_quant_down"] = hbm_entry(timer.avg_ms("swiglu_quant_down"), m * k * 5 + m * k // 128 * 4)
+        r["quant_w_experts"] = hbm_entry(timer.avg_ms("quant_w_experts"),
+                                         E * (2 * 768 * 2048 + 2048 * 768) * W_BPE)
+        out[mname] = r
+        del step
+        torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = cpu_moe()
+    return out
+
+
+def row_tiny(fp8bs, dev, steps, warmup, cpu):
+    """d6: the tiny linear layer (X [256, 512], W [512, 512], seed 0): latency of
+    quant_act_1x128 + quant_w_128x128 + fp8_block_gemm, reported, not rooflined."""
+    import synth
+    import torch
+    M, N, K = 256, 512, 512
+    x = bf16_dev(synth.activations(M, K), dev)
+    w = bf16_dev(synth.weights(N, K), dev)
+    xq, xs = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((M, K // 128), dtype=torch.float32,
+                                                                              device=dev)
+    wq, ws = torch.empty((N, K), dtype=torch.uint8, device=dev), torch.empty((N // 128, K // 128),
+                                                                              dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    timer = KernelTimer()
+    reps = max(100, 5 * steps)
+    for r in range(warmup + reps):
+        t = timer if r >= warmup else None
+
+        def layer():
+            fp8bs.quant_act_1x128(x, 0, out=(xq, xs))
+            fp8bs.quant_w_128x128(w, 0, out=(wq, ws))
+            fp8bs.fp8_block_gemm(xq, xs, wq, ws, out=y)
+        maybe(t, "layer", layer)
+        maybe(t, "gemm", lambda: fp8bs.fp8_block_gemm(xq, xs, wq, ws, out=y))
+    torch.cuda.synchronize()
+    lm, lmin = timer.spread("layer")
+    gm, gmin = timer.spread("gemm")
+    out = {"config": "X [256,512], W [512,512], seed 0, EXACT: quant_act_1x128 + quant_w_128x128 + fp8_block_gemm "
+                     "(bf16 out), three launches on one stream, %d timed repetitions" % reps,
+           "latency_us": {"layer_median": round(lm * 1e3, 2), "layer_min": round(lmin * 1e3, 2),
+                          "gemm_median": round(gm * 1e3, 2), "gemm_min": round(gmin * 1e3, 2)},
+           "flops": 2.0 * M * N * K}
+    if cpu:
+        out["cpu_baseline"] = cpu_tiny()
+    return out
+
+
+def row_gemm_quant(fp8bs, dev, steps, warmup, cpu):
+    """NEXT-2: a GEMM whose output feeds another FP8 GEMM, at the o_proj and QKV shapes (M = 8192):
+    fp8_block_gemm then quant_act_1x128 of its bf16 output, against fp8_block_gemm_quant (codes and
+    scales from the GEMM's epilogue), with and without the bf16 output."""
+    import synth
+    import torch
+    out = {"config": "M=8192, EXACT: 'separate' = fp8_block_gemm (bf16 Y) + quant_act_1x128(Y); 'fused' = "
+                     "fp8_block_gemm_quant with Y; 'fused_codes_only' = fp8_block_gemm_quant without Y"}
+    for name, N, K in (("o_proj", 4096, 4096), ("qkv", 6144, 4096)):
+        M = 8192
+        xq, xs = fp8bs.quant_act_1x128(synth.activations_dev(M, K, dev, sub=synth.SUB_X + 80))
+        wq, ws = fp8bs.quant_w_128x128(synth.weights_dev(N, K, dev, sub=synth.sub_layer(80)))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        ys = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+        timer = KernelTimer()
+
+        def sep():
+            fp8bs.fp8_block_gemm(xq, xs, wq, ws, out=y)
+            fp8bs.quant_act_1x128(y, 0, out=(yq, ys))
+        for r in range(warmup + steps):
+            t = timer if r >= warmup else None
+            maybe(t, "separate", sep)
+            maybe(t, "fused", lambda: fp8bs.fp8_block_gemm_quant(xq, xs, wq, ws, 0, out=(y, yq, ys)))
+            maybe(t, "fused_codes_only", lambda: fp8bs.fp8_block_gemm_quant(xq, xs, wq, ws, 0, out=(None, yq, ys)))
+        torch.cuda.synchronize()
+        fl = 2.0 * M * N * K
+        out[name] = {k: {**mfma_entry(timer.avg_ms(k), fl), "median_ms": round(timer.spread(k)[0], 4)}
+                     for k in ("separate", "fused", "fused_codes_only")}
+        out[name]["fused_saving_frac"] = round(1 - timer.avg_ms("fused") / timer.avg_ms("separate"), 4)
+        del xq, xs, wq, ws, y, yq, ys
+    torch.cuda.empty_cache()
+    return out
+
+
+ATT = dict(B=64, T=4096, Hq=32, Hkv=8)  # decode attention: 64 sequences, 4096 cached tokens, Llama-3.1-8B heads
+
+
+def cpu_attention(target_s=CPU_TARGET_S):
+    """The oracle's fp64 attention over the FP8 cache: sequences of 4096 tokens, 32 / 8 heads."""
+    import oracle
+    import synth
+    T, Hq, Hkv = ATT["T"], ATT["Hq"], ATT["Hkv"]
+    k = synth.activations(T, Hkv * 128, sub=synth.SUB_X)
+    v = synth.activations(T, Hkv * 128, sub=synth.SUB_W)
+    kq, ks = oracle.quant_act_1x128(k)
+    vq, vs = oracle.quant_act_1x128(v)
+    q1 = synth.activations(Hq, 128, sub=synth.SUB_DY)
+
+    def make(n):
+        b = max(1, min(64, n))
+        shape = (b, T, Hkv)
+        kq_b = np.ascontiguousarray(np.broadcast_to(kq.reshape(1, T, Hkv, 128), shape + (128,)))
+        vq_b = np.ascontiguousarray(np.broadcast_to(vq.reshape(1, T, Hkv, 128), shape + (128,)))
+        ks_b = np.ascontiguousarray(np.broadcast_to(ks.reshape(1, T, Hkv), shape))
+        vs_b = np.ascontiguousarray(np.broadcast_to(vs.reshape(1, T, Hkv), shape))
+        q = np.ascontiguousarray(np.broadcast_to(q1.reshape(1, Hq, 128), (b, Hq, 128)))
+        lens = np.full(b, T, np.int32)
+        return (lambda: oracle.kv_attention_decode(q, kq_b, ks_b, vq_b, vs_b, lens, 0.088388)), b
+    per_seq = T * Hkv * 2 * (128 + 4)
+    return cpu_row(make, lambda b: b * per_seq / 1e9, "GB/s",
+                   lambda b, dt: "kv_attention_decode of %d sequences x %d cached tokens (32 query / 8 key-value "
+                                 "heads), %.2f s wall" % (b, T, dt), 1, 64, target_s)
+
+
+def row_attention(fp8bs, dev, steps, warmup, cpu):
+    """NEXT-4: decode attention over the FP8 KV cache, one layer: 64 sequences x 4096 cached
+    tokens, 32 query / 8 key-value heads of dim 128; the cache written by quant_act_1x128."""
+    import synth
+    import torch
+    B, T, Hq, Hkv = ATT["B"], ATT["T"], ATT["Hq"], ATT["Hkv"]
+    k = synth.activations_dev(B * T, Hkv * 128, dev, sub=synth.SUB_X + 70)
+    v = synth.activations_dev(B * T, Hkv * 128, dev, sub=synth.SUB_W + 70)
+    kq, ks = fp8bs.quant_act_1x128(k)
+    vq, vs = fp8bs.quant_act_1x128(v)
+    del k, v
+    kq, vq = kq.view(B, T, Hkv, 128), vq.view(B, T, Hkv, 128)
+    ks, vs = ks.view(B, T, Hkv), vs.view(B, T, Hkv)
+    q = synth.activations_dev(B * Hq, 128, dev, sub=synth.SUB_DY + 70).view(B, Hq, 128)
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, fp8bs.kv_attention_workspace_size(B, T, Hq, Hkv)), dtype=torch.uint8, device=dev)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    timer = KernelTimer()
+    for r in range(warmup + steps):
+        t = timer if r >= warmup else None
+        scrub.fill_(r & 0xFF)   # the 554 MB cache is larger than the 256 MB infinity cache anyway
+        maybe(t, "attn", lambda: fp8bs.fp8_kv_attention_decode(q, kq, ks, vq, vs, lens, 0.088388, out=out,
+                                                                workspace=ws))
+    torch.cuda.synchronize()
+    ta = timer.avg_ms("attn")
+    med, mn = timer.spread("attn")
+    nbytes = 2 * B * T * Hkv * (128 + 4) + B * Hq * 128 * 2 * 2 + B * 4
+    out_d = {"config": "one layer: %d sequences x %d cached tokens, %d query / %d key-value heads of dim 128, "
+                       "E4M3 cache with one fp32 scale per token and head, bf16 out" % (B, T, Hq, Hkv),
+             "attention": {**hbm_entry(ta, nbytes), "median_ms": round(med, 4), "min_ms": round(mn, 4),
+                           "splits_workspace_bytes": fp8bs.kv_attention_workspace_size(B, T, Hq, Hkv),
+                           "roofline": roof_hbm("fp8bs::kv_attn_decode_kernel<4>", ta, nbytes)},
+             "bf16_cache_roofline_ms": round((nbytes + 2 * B * T * Hkv * 124) / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
+    del kq, vq, ks, vs, scrub
+    torch.cuda.empty_cache()
+    if cpu:
+        out_d["cpu_baseline"] = cpu_attention()
+    return out_d
 
 
 # ---------------------------------------------------------------------------
@@ -590,7 +1076,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "recal", "decode", "moe", "train"])
+    ap.add_argument("--workload", default="all", choices=["all", "dense", "recal", "decode", "moe", "train"])
     ap.add_argument("--mode", type=int, default=0, help="scale mode: 0 EXACT, 1 POW2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -616,6 +1102,36 @@ def main():
     common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
 
+    if args.workload == "all":
+        # the headline: the 8B-shaped dense layer (EXACT); then every other row, each timed on its own
+        cpu_on = not args.no_cpu_baseline
+        bufs = dense_data(dev)
+        flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
+        ms = timed_loop(dense_step(fp8bs, bufs, 0), args.steps, args.warmup, timer)
+        kernels, roof = summarize_dense(bufs, timer)
+        out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
+               "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
+               "config": {"workload": "8B-shaped dense layer at M=8192 tokens: recalibrate 4 weights (128x128, one "
+                                      "batched launch), quantize 4 inputs (1x128), GEMMs QKV K4096 N6144, gate+up "
+                                      "K4096 N28672, down K14336 N4096, o_proj K4096 N4096",
+                          "scale_mode": "exact", "out_dtype": "bf16", "gemm_flops_per_step": flops},
+               "roofline": roof, "kernels": with_spread(kernels, timer)}
+        log("d3 dense, POW2")
+        rows = {"d3_dense_pow2": row_dense_pow2(fp8bs, bufs, args.steps, args.warmup)}
+        del bufs
+        torch.cuda.empty_cache()
+        if cpu_on:
+            log("timing the oracle: dense")
+            out["cpu_baseline"] = cpu_dense()
+        for key, fn in (("d1_recal", row_recal), ("d2_quant_act", row_quant_act), ("d4_decode", row_decode),
+                        ("d5_moe", row_moe), ("d6_tiny", row_tiny), ("next2_gemm_quant", row_gemm_quant),
+                        ("next4_kv_attention", row_attention)):
+            log("row " + key)
+            rows[key] = fn(fp8bs, dev, args.steps, args.warmup, cpu_on)
+            torch.cuda.empty_cache()
+        out["rows"] = rows
+        print(json.dumps(out), flush=True)
+        return
     if args.workload == "dense":
         step, bufs, flops = dense_workload(fp8bs, dev, args.mode)
         ms = timed_loop(step, args.steps, args.warmup, timer)

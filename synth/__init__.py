@@ -28,7 +28,9 @@ values are synthetic):
   ordered by token, and the group offsets are the prefix sums of the counts.
 
 Every generator is keyed by (seed, sub-stream) through numpy's PCG64, so the
-same bytes reach the GPU and the oracle.
+same bytes reach the GPU and the oracle.  The ``*_dev`` generators draw the
+same recipes directly on a device with torch's seeded device generator: they
+serve the benchmark's large timing inputs, whose bytes no oracle compares.
 """
 
 from __future__ import annotations
@@ -99,6 +101,28 @@ def expert_weights(E: int, N: int, K: int, seed: int = SEED, sub: int = SUB_W,
     w = g.standard_normal((E, N, K), dtype=np.float32)
     w *= np.float32(std)
     return f32_to_bf16_bits(w)
+
+
+def _dev_gen(seed: int, sub: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + int(sub))
+    return g
+
+
+def activations_dev(M: int, K: int, device, seed: int = SEED, sub: int = SUB_X,
+                    outlier_p: float = 1e-3, outlier_mul: float = 50.0) -> torch.Tensor:
+    """bf16 tensor [M, K] on ``device``: the activation recipe, drawn on the device."""
+    g = _dev_gen(seed, sub, device)
+    x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
+    hit = torch.rand((M, K), generator=g, device=device, dtype=torch.float32) < outlier_p
+    x = torch.where(hit, x * outlier_mul, x)
+    return x.to(torch.bfloat16)
+
+
+def weights_dev(N: int, K: int, device, seed: int = SEED, sub: int = SUB_W, std: float = 0.02) -> torch.Tensor:
+    """bf16 tensor [N, K] on ``device``: std * N(0, 1), drawn on the device."""
+    g = _dev_gen(seed, sub, device)
+    return (torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
 
 
 def moe_routing(tokens: int, experts: int, topk: int, seed: int = SEED,

@@ -130,3 +130,28 @@ def test_kernel_timer_median_and_min():
     assert kt.spread("k") == (2.5, 1.0)
     kt.pairs["odd"] = [(Ev(1.0), Ev(1.0 + d)) for d in (5.0, 4.0, 6.0)]
     assert kt.spread("odd") == (5.0, 4.0)
+
+
+def test_roofline_helpers(bench):
+    r = bench.roof_hbm("k", 1.0, 4e9)
+    assert r["bound"] == "hbm" and r["achieved"] == pytest.approx(4000.0) and r["frac"] == pytest.approx(0.5)
+    r = bench.roof_mfma("k", 1.0, 2.5e12)
+    assert r["bound"] == "mfma" and r["frac"] == pytest.approx(0.5)
+    # the bound that binds: bytes at 8 TB/s against FLOPs at 5 PFLOP/s
+    assert bench.roof_binding("k", 1.0, 1e12, 1e9)["bound"] == "mfma"   # 200 us of MFMA vs 125 us of HBM
+    assert bench.roof_binding("k", 1.0, 1e11, 1e9)["bound"] == "hbm"
+
+
+@pytest.mark.parametrize("name", ["cpu_recal", "cpu_quant_act", "cpu_dense", "cpu_decode", "cpu_moe", "cpu_tiny",
+                                  "cpu_attention"])
+def test_cpu_baselines_run(bench, name):
+    """Every row's oracle baseline runs on the host and reports both thread counts."""
+    kw = {"target_s": 0.01}
+    if name == "cpu_moe":
+        kw["experts"] = 2
+    cb = getattr(bench, name)(**kw)
+    assert cb["kind"] == "oracle" and cb["cores"] >= 1
+    assert cb["value"] > 0 and cb["value_1thread"] > 0
+    assert isinstance(cb["sample"], str) and isinstance(cb["sample_1thread"], str)
+    import oracle
+    assert oracle.max_threads() == cb["cores"]   # the thread count is restored
