@@ -195,6 +195,21 @@ __device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x
     return pack4_e4m3(x0 / s, x1 / s, x2 / s, x3 / s);
 }
 
+// The IEEE-division path of quant4 out of line, for callers that inline many
+// quant4 calls on a path that is rarely taken (the GEMM epilogue): it keeps
+// their code, and the instruction cache it occupies, small.
+__device__ __noinline__ uint32_t quant4_ieee(float x0, float x1, float x2, float x3, float s)
+{
+    return pack4_e4m3(x0 / s, x1 / s, x2 / s, x3 / s);
+}
+
+// quant4's fast path alone (the caller has checked bq.fast).
+template <int MODE>
+__device__ __forceinline__ uint32_t quant4_fast(float x0, float x1, float x2, float x3, const BlockQuant<MODE> &bq)
+{
+    return pack4_e4m3(bq.q_fast(x0), bq.q_fast(x1), bq.q_fast(x2), bq.q_fast(x3));
+}
+
 // 8 bf16 values (one 16-byte chunk) -> 8 codes.
 template <int MODE>
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, const BlockQuant<MODE> &bq)

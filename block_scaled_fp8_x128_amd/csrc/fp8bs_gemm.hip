@@ -781,7 +781,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     // a ring of three (the group being multiplied and the next two).
     v8i bx[C::TM];
     v8i awq[3];
-    float sc[C::TM];
+    float sc[C::TM];   // the step's scale product per row tile (POW2: the activation scale alone)
+    float sw_cur = 1.f; // the step's weight scale (POW2)
     auto ws_of = [&](const TileGeo &g) {
         return (const CONST_AS float *)(g.ws + ((g.n0 + wn * C::WN) / 128) * KB);
     };
@@ -827,15 +828,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         v4f part[2];
         float xs_next[C::TM];
         float sw_next = 0.f;
-        // POW2: the E8M0 code of each row tile's scale product (its biased
-        // exponent; the product of two powers of two is exact in fp32).  Lane
-        // l's scale applies to the activation row l % 16 whose fragment it
-        // holds, which is the row its scale product belongs to.
+        // POW2: each factor of the scale product goes to its own operand's
+        // E8M0 scale, as its biased exponent (exact for every power of two
+        // from 2^-127 up; the product itself may lie below fp32's normal
+        // range): the step's weight scale on the weight operand, uniform over
+        // the wave, and the activation row's scale on the activation operand --
+        // lane l holds the fragment of row l % 16, whose scale it passes.
         int e8[C::TM];
+        int e8w = 127;
         if constexpr (POW2) {
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
                 e8[i] = (int)(__builtin_bit_cast(uint32_t, sc[i]) >> 23);
+            e8w = (int)(__builtin_bit_cast(uint32_t, sw_cur) >> 23);
         }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
@@ -882,7 +887,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             for (int i = 0; i < C::TM; ++i) {
                 const int t = j * C::TM + i;
                 if constexpr (POW2)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], acc[i][j], 0, 0, 0, 127, 0,
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], acc[i][j], 0, 0, 0, e8w, 0,
                                                                                  e8[i]);
                 else
                     part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -913,9 +918,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         }
         if constexpr (!POW2)
             rescale(C::TM * C::TN - 1, part[(C::TM * C::TN - 1) & 1]);
+        // (POW2 keeps the two factors apart for the E8M0 operands)
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
-            sc[i] = xs_next[i] * sw_next;
+            sc[i] = POW2 ? xs_next[i] : xs_next[i] * sw_next;
+        sw_cur = sw_next;
         // the next step's groups 0 and 1 were read into slots TN % 3 and
         // (TN + 1) % 3; move them to slots 0 and 1
         const v8i n0 = awq[C::TN % 3], n1 = awq[(C::TN + 1) % 3];
@@ -980,11 +987,25 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                     bq.init(amax_value(mx));
                     // codes staged by rows (row fr: bytes 16 j + 4 fg), then read back
                     // 16 bytes per lane, 8 lanes per 128-byte row
+                    // one wave-uniform test for the rare blocks outside the fast
+                    // quotient's window (then every lane takes IEEE division,
+                    // which is exact for all), instead of a divergent branch per
+                    // call: it keeps the epilogue's code, and its share of the
+                    // instruction cache, small
+                    if (__builtin_amdgcn_ballot_w64(!bq.fast) == 0) {
 #pragma unroll
-                    for (int j = 0; j < C::TN; ++j) {
-                        const u32x2 w = bw_of(j);
-                        *(uint32_t *)(epi_lds + fr * C::EPI_RS + j * 16 + fg * 4) =
-                            quant4<QM>(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), bq);
+                        for (int j = 0; j < C::TN; ++j) {
+                            const u32x2 w = bw_of(j);
+                            *(uint32_t *)(epi_lds + fr * C::EPI_RS + j * 16 + fg * 4) =
+                                quant4_fast<QM>(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), bq);
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < C::TN; ++j) {
+                            const u32x2 w = bw_of(j);
+                            *(uint32_t *)(epi_lds + fr * C::EPI_RS + j * 16 + fg * 4) =
+                                quant4_ieee(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), bq.s);
+                        }
                     }
                     const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.yq + g.row_begin * N + g.n0, rows * N);
 #pragma unroll
@@ -1075,7 +1096,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         const float sw = WROW ? 1.0f : ws_of(ct)[ct.kb0];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
-            sc[i] = *(const float *)(lds + so + i * 64) * sw;
+            sc[i] = POW2 ? *(const float *)(lds + so + i * 64) : *(const float *)(lds + so + i * 64) * sw;
+        sw_cur = sw;
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
             bx[i] = frag(lds + xo[0] + i * 2048, lds + xo[1] + i * 2048);

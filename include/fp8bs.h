@@ -328,14 +328,16 @@ FP8BS_API int fp8_block_grouped_gemm(const void *xq, const float *xs, const void
  * quantizers).  Arguments, layouts, workspace and errors are exactly those of
  * fp8_block_gemm and fp8_block_grouped_gemm.
  *
- * Precondition: every xs and ws entry is a power of two, and every product
- * xs[m, kb] * ws[n/128, kb] is a normal fp32 number (>= 2^-126), which holds
- * for POW2-quantized data of any ordinary magnitude.  Each K block's scale
- * product 2^e is then exact, and on the large-tile kernels it is handed to
- * the matrix cores' E8M0 block-scale operand: the MFMA accumulates 2^e * P
- * directly, with no fp32 rescale pass.  Only the exponent of each scale
- * product is used there; with scales that break the precondition the result
- * is unspecified (it is never a memory fault).  Results agree with
+ * Precondition: every xs and ws entry is a power of two no smaller than
+ * 2^-127 (the E8M0 range; POW2 quantization gives that for every block whose
+ * amax is at least 448 * 2^-127, about 2.6e-36).  On the large-tile kernels
+ * each K block's two scales go to the matrix cores' E8M0 block-scale
+ * operands, the weight scale on the weight operand and the activation row's
+ * scale on the activation operand, so the MFMA accumulates
+ * 2^(ex + ew) * P directly, exactly, with no fp32 rescale pass, even where
+ * the product of the two scales lies below fp32's normal range.  Only each
+ * scale's exponent is used there; with scales that break the precondition
+ * the result is unspecified (it is never a memory fault).  Results agree with
  * fp8_block_gemm on the same operands to within fp32 rounding of the
  * accumulation order; the bf16 output is again the round-to-nearest-even of
  * the fp32 output of the same call shape.

@@ -114,6 +114,28 @@ def test_gemm_integer_special_case(fp8bs):
     assert np.array_equal(host(y), 4 * ref)
 
 
+@pytest.mark.parametrize("shape", [(300, 512, 1024), (4096, 4096, 256)], ids=["split_128x256", "256x256"])
+def test_gemm_pow2_scale_products_below_normal_range(fp8bs, orc, shape):
+    """Power-of-2 scales whose products fall below fp32's normal range (2^-64 * 2^-64 = 2^-128), or
+    mix tiny and large factors, down to the smallest E8M0 scale 2^-127: each factor rides its own
+    operand's E8M0 scale, so the POW2 entry point matches the oracle (a single E8M0 code for the
+    product read 2^-128 as 2^-127, off by a factor of 2)."""
+    M, N, K = shape
+    g = np.random.default_rng(M + K)
+    xq = g.integers(0, 256, (M, K), dtype=np.uint8)
+    wq = g.integers(0, 256, (N, K), dtype=np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x3F
+    wq[(wq & 0x7F) == 0x7F] = 0x3F
+    for ex, ew in ((-64, -64), (-100, 60), (-127, 20), (40, -127), (-70, -50)):
+        jx = g.integers(-2, 3, (M, K // 128))
+        jw = g.integers(-2, 3, (N // 128, K // 128))
+        xs = np.ldexp(1.0, np.maximum(ex + jx, -127)).astype(np.float32)
+        ws = np.ldexp(1.0, np.maximum(ew + jw, -127)).astype(np.float32)
+        say("fp8_block_gemm_pow2 M=%d N=%d K=%d scale exponents around %d, %d" % (M, N, K, ex, ew))
+        y = fp8bs.fp8_block_gemm_pow2(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), out_dtype=torch.float32)
+        gemm_gate("Y fp32 (pow2 entry)", host(y), orc.gemm_full(xq, xs, wq, ws))
+
+
 def test_gemm_empty(fp8bs):
     xq = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
     xs = torch.empty((0, 2), dtype=torch.float32, device="cuda")
