@@ -38,6 +38,9 @@ Tool modes (no GPU work of their own):
   --copy-calibration   after the timed steps, copy a 1 GiB buffer three times
                        (a plain copy kernel of known size, the reference for
                        scaling rocprofv3 FETCH_SIZE / WRITE_SIZE);
+  --summarize-trace TRACE_DB OUT_MD  summarize a rocprofv3 --kernel-trace
+                       database of the default run (per-kernel statistics and
+                       the headline kernel's timed dispatches);
   --summarize-pmc FETCH_DB WRITE_DB  turn two rocprofv3 --pmc databases of
                        `bench.py --copy-calibration` into the traffic record
                        profiles/<kernel>_traffic.json that the roofline reads.
@@ -69,7 +72,7 @@ COPY_BYTES = 1 << 30
 # Dominant kernel of each workload: (kernel-name prefix in a rocprofv3 trace,
 # source file, traffic record under profiles/).
 DOMINANT = {
-    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, false>", GEMM_SRC,
+    "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, false, 0>", GEMM_SRC,
               "gemm_dma_256x256_dense_m8192_traffic.json"),
     "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
     # the grouped gate+up call: its row-tile table, the 256-row pass and the short-tile pass
@@ -283,7 +286,7 @@ def summarize_train(bufs, timer):
     if sum(w_ms) > d_ms:
         mean_ms, mean_flops = sum(w_ms) / len(w_ms), sum(w_flops) / len(w_flops)
         ach = mean_flops / (mean_ms * 1e-3) / 1e12
-        roof = {"kernel": "fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, true> (weight "
+        roof = {"kernel": "fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, true, 0> (weight "
                           "gradients of QKV, gate+up, down, o_proj over 8192 tokens)", "bound": "mfma",
                 "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,
@@ -729,7 +732,7 @@ def row_dense_pow2(fp8bs, bufs, steps, warmup):
     timer = KernelTimer()
     ms = timed_loop(dense_step(fp8bs, bufs, 1), steps, warmup, timer)
     kernels, roof = summarize_dense(bufs, timer)
-    roof["kernel"] = roof["kernel"].replace("false, false, false, false, false>", "false, false, false, true, false>")
+    roof["kernel"] = roof["kernel"].replace("false, false, false, false, false, 0>", "false, false, false, true, false, 0>")
     roof["traffic"], roof["traffic_source"] = None, None
     flops = sum(2.0 * b["M"] * b["N"] * b["K"] for b in bufs)
     return {"ms_per_step": round(ms, 4), "TFLOP/s_step": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -1067,6 +1070,49 @@ def summarize_pmc(fetch_db, write_db, workload, command, out=None):
     return rec
 
 
+def summarize_trace(db, command, steps, warmup, out):
+    """Markdown summary of a rocprofv3 --kernel-trace database of `bench.py`: per kernel the
+    dispatch count and duration statistics, then the headline kernel's timed dispatches (the
+    dense layer's four GEMMs of steps warmup .. warmup + steps - 1, in dispatch order), the
+    figures the line's roofline divides by."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select s.display_name, d.start, d.end from rocpd_kernel_dispatch d join kernel_symbols s "
+                     "on d.kernel_id = s.id order by d.start").fetchall()
+    per = {}
+    for name, t0, t1 in rows:
+        per.setdefault(name, []).append((t1 - t0) / 1e3)
+    srcs = ["block_scaled_fp8_x128_amd/csrc/" + f for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp8_x128_amd",
+                                                                                      "csrc")))]
+    lines = ["# rocprofv3 kernel trace: `bench.py` default run", "",
+             "Command (on the MI355X box, from the repository root):", "", "    " + command, "",
+             "Sources at the time of the trace (sha256, first 16 hex digits):", ""]
+    lines += ["- `%s`: %s" % (f, src_hash(os.path.join(ROOT, f))) for f in srcs]
+    lines += ["- `bench.py`: %s" % src_hash(os.path.join(ROOT, "bench.py")), ""]
+    dom = DOMINANT["dense"][0]
+    heads = [d for (n, t0, t1), d in zip(rows, [(r[2] - r[1]) / 1e3 for r in rows])
+             if n.startswith("void " + dom) or n.startswith(dom)]
+    first = heads[4 * warmup: 4 * (warmup + steps)]
+    if first:
+        srt = sorted(first)
+        lines += ["## Headline kernel, timed dispatches", "",
+                  "`%s`: the dense layer's QKV, gate+up, down and o_proj GEMMs of the %d timed steps (the first %d "
+                  "dispatches of the kernel are the warm-up steps)." % (dom, steps, 4 * warmup), "",
+                  "| dispatches | mean us | median us | min us | max us |", "|---|---|---|---|---|",
+                  "| %d | %.1f | %.1f | %.1f | %.1f |" % (len(first), sum(first) / len(first), srt[len(srt) // 2],
+                                                         srt[0], srt[-1]), ""]
+    lines += ["## All kernels", "", "| kernel | calls | total ms | mean us | median us | min us |",
+              "|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        v2 = sorted(v)
+        short = name.replace("void ", "").split("(")[0].replace("|", "/")
+        lines.append("| `%s` | %d | %.3f | %.1f | %.1f | %.1f |" % (short, len(v), sum(v) / 1e3, sum(v) / len(v),
+                                                                  v2[len(v2) // 2], v2[0]))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:40]))
+
+
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
@@ -1082,9 +1128,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     ap.add_argument("--pmc-command", default="", help="the profiled command, recorded with --summarize-pmc")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DB", "OUT_MD"),
+                    help="summarize a rocprofv3 --kernel-trace database of this script's default run")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.pmc_command, args.steps, args.warmup, args.summarize_trace[1])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
