@@ -27,8 +27,10 @@ Workloads (--workload):
          data-gradient GEMM dX = dY W, the quantization of dY^T and X^T along
          the tokens and the weight-gradient GEMM dW = dY^T X.
   moe    MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens
-         routed top-8: expert-weight recalibration, quantization of the
-         gate+up and down inputs, the two grouped GEMMs.
+         routed top-8: expert-weight recalibration, the dispatch (each token
+         row quantized once and written to its 8 expert rows), the grouped
+         gate+up GEMM, the gated activation quantized for the down input, the
+         grouped down GEMM.
 Prints ONE JSON line.  `value` is GEMM TFLOP/s over the whole step
 (quantizers included) except for `recal` (GB/s).  Per-kernel times come from
 HIP events recorded on the stream the library launches on (torch's current
@@ -459,9 +461,11 @@ def moe_workload(fp8bs, dev, mode):
     row_token, offs = synth.moe_routing(T, E, TOPK)
     Mt = int(offs[-1])
     log("MoE: %d routed rows, per-expert rows min %d max %d" % (Mt, int(np.diff(offs).min()), int(np.diff(offs).max())))
-    # the dispatch: each routed row reads its token's row (quantized on the way, in expert order)
+    # the dispatch: each token row is read and quantized once and written to its 8 expert rows
+    # (the gather form, timed beside the step, reads each token row once per routed copy)
     xt = synth.activations_dev(T, H, dev, sub=synth.SUB_X)
     rows_d = torch.from_numpy(np.ascontiguousarray(row_token, dtype=np.int32)).to(dev)
+    dest_d = torch.from_numpy(synth.moe_dest(row_token, T, TOPK)).to(dev)
     w1 = synth.weights_dev(E * 2 * F, H, dev, sub=synth.SUB_W)
     w2 = synth.weights_dev(E * H, F, dev, sub=synth.SUB_W + 1)
     offs_d = torch.from_numpy(offs).to(dev)
@@ -483,8 +487,9 @@ def moe_workload(fp8bs, dev, mode):
         maybe(timer, "quant_w_experts", lambda: fp8bs.quant_w_128x128_batched([w1, w2], mode,
                                                                                outs=[(b["w1q"], b["w1s"]),
                                                                                      (b["w2q"], b["w2s"])]))
-        maybe(timer, "quant_act_gather_gate_up", lambda: fp8bs.quant_act_1x128_gather(xt, rows_d, mode,
-                                                                                    out=(b["x1q"], b["x1s"])))
+        maybe(timer, "quant_act_scatter_gate_up", lambda: fp8bs.quant_act_1x128_scatter(xt, dest_d, Mt, mode,
+                                                                                      out=(b["x1q"], b["x1s"])))
+
         maybe(timer, "grouped_gate_up", lambda: grouped(
             b["x1q"], b["x1s"], b["w1q"].view(E, 2 * F, H), b["w1s"].view(E, 2 * F // 128, H // 128), offs_d,
             out=b["y1"], workspace=b["wk1"]))
@@ -496,6 +501,13 @@ def moe_workload(fp8bs, dev, mode):
 
     shapes = {"gate_up": (Mt, 2 * F, H), "down": (Mt, H, F)}
     flops = sum(2.0 * m * n * k for m, n, k in shapes.values())
+
+    def gather_form(timer, reps):
+        # the gather form of the same dispatch (same outputs), timed after the steps for comparison
+        for _ in range(reps):
+            maybe(timer, "quant_act_gather_gate_up", lambda: fp8bs.quant_act_1x128_gather(xt, rows_d, mode,
+                                                                                        out=(b["x1q"], b["x1s"])))
+    step.gather_form = gather_form
     return step, shapes, flops, E
 
 
@@ -801,6 +813,9 @@ def row_moe(fp8bs, dev, steps, warmup, cpu):
         timer = KernelTimer()
         step, shapes, flops, E = moe_workload(fp8bs, dev, mode)
         ms = timed_loop(step, steps, warmup, timer)
+        step.gather_form(None, 2)
+        step.gather_form(timer, steps)
+        torch.cuda.synchronize()
         r = {"ms_per_step": round(ms, 4), "TFLOP/s_step": round(flops / (ms * 1e-3) / 1e12, 2)}
         traffic, tsrc = traffic_for("moe") if mode == 0 else (None, None)
         for name, (m, n, k) in shapes.items():
@@ -813,8 +828,8 @@ def row_moe(fp8bs, dev, steps, warmup, cpu):
                                     "roofline": roof_binding("fp8_block_grouped_gemm%s %s" %
                                                              ("_pow2" if mode else "", name), t, fl, nbytes, *tr)}
         m, _, k = shapes["gate_up"]
-        r["quant_act_gather_gate_up"] = hbm_entry(timer.avg_ms("quant_act_gather_gate_up"),
-                                                  T_TOKENS * k * 2 + m * 4 + m * k + m * k // 128 * 4)
+        for dname in ("quant_act_scatter_gate_up", "quant_act_gather_gate_up"):
+            r[dname] = hbm_entry(timer.avg_ms(dname), T_TOKENS * k * 2 + m * 4 + m * k + m * k // 128 * 4)
         m, _, k = shapes["down"]
         r["swiglu_quant_down"] = hbm_entry(timer.avg_ms("swiglu_quant_down"), m * k * 5 + m * k // 128 * 4)
         r["quant_w_experts"] = hbm_entry(timer.avg_ms("quant_w_experts"),
@@ -1023,7 +1038,8 @@ def _grouped_gate_up_calls(db, counter):
             cur.append(v)
         else:
             cur = None
-            after_quant = "quant_act_kernel" in k or "quant_act_gather_kernel" in k
+            after_quant = any(q in k for q in ("quant_act_kernel", "quant_act_gather_kernel",
+                                               "quant_act_scatter_kernel"))
     if not calls:
         raise SystemExit("no grouped gate+up call found in the counter database")
     return sum(sum(c) for c in calls) / len(calls), len(calls)
@@ -1265,15 +1281,18 @@ def main():
     else:
         step, shapes, flops, E = moe_workload(fp8bs, dev, args.mode)
         ms = timed_loop(step, args.steps, args.warmup, timer)
+        step.gather_form(None, 2)
+        step.gather_form(timer, args.steps)
+        torch.cuda.synchronize()
         kernels = {}
         for name, (m, n, k) in shapes.items():
             t = timer.avg_ms("grouped_" + name)
             nbytes = m * k + m * k // 128 * 4 + E * n * k * (1 + 4 / 16384) + m * n * 2
             kernels["grouped_" + name] = {**mfma_entry(t, 2.0 * m * n * k), **hbm_entry(t, nbytes)}
         m, _, k = shapes["gate_up"]
-        # dispatch quantizer: the token rows read once (T x K bf16), the row indices, codes and scales written
-        kernels["quant_act_gather_gate_up"] = hbm_entry(timer.avg_ms("quant_act_gather_gate_up"),
-                                                        T_TOKENS * k * 2 + m * 4 + m * k + m * k // 128 * 4)
+        # dispatch quantizer: the token rows read once (T x K bf16), the routing, codes and scales written
+        for dname in ("quant_act_scatter_gate_up", "quant_act_gather_gate_up"):
+            kernels[dname] = hbm_entry(timer.avg_ms(dname), T_TOKENS * k * 2 + m * 4 + m * k + m * k // 128 * 4)
         # gated activation + quantizer: 2 bf16 in, 1 code out per element of h, one fp32 per 128
         m, _, k = shapes["down"]
         kernels["swiglu_quant_down"] = hbm_entry(timer.avg_ms("swiglu_quant_down"), m * k * 5 + m * k // 128 * 4)
@@ -1295,7 +1314,7 @@ def main():
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "MoE layer: 128 experts, hidden 2048, expert FFN 768, 8192 tokens top-8 "
-                                      "(65536 rows); the dispatch quantizing token rows into expert order, grouped "
+                                      "(65536 rows); the dispatch quantizing each token row once into its 8 expert rows, grouped "
                                       "gate+up K2048 N1536, the gated activation quantized for the down projection, "
                                       "grouped down K768 N2048"},
                "roofline": {"kernel": "fp8_block_grouped_gemm gate+up", **roof,

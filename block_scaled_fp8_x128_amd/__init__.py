@@ -38,6 +38,7 @@ EXPORTS = (
     "quant_act_1x128_t",
     "quant_act_1x128_dual",
     "quant_act_1x128_gather",
+    "quant_act_1x128_scatter",
     "swiglu_quant_1x128",
     "quant_w_128x128",
     "quant_w_128x128_batched",
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.quant_act_1x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
         L.swiglu_quant_1x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_act_1x128_gather.argtypes = [P, I64, I64, P, I64, P, P, I32, P]
+        L.quant_act_1x128_scatter.argtypes = [P, I64, I64, P, I64, I64, P, P, I32, P]
         L.fp8_block_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
@@ -112,7 +114,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_status_string.restype = ctypes.c_char_p
         L.fp8bs_abi_version.restype = I32
         for fn in ("quant_act_1x128", "quant_act_1x128_t", "quant_act_1x128_dual", "swiglu_quant_1x128",
-                   "quant_act_1x128_gather",
+                   "quant_act_1x128_gather", "quant_act_1x128_scatter",
                    "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
@@ -245,6 +247,24 @@ def quant_act_1x128_gather(x: torch.Tensor, rows: torch.Tensor, mode: int = SCAL
     xq, xs = _pair_out(out, M, K, x.device)
     _check("quant_act_1x128_gather", lib().quant_act_1x128_gather(_ptr(x), T, K, _ptr(rows), M, _ptr(xq), _ptr(xs),
                                                                  int(mode), _stream(x)))
+    return xq, xs
+
+
+def quant_act_1x128_scatter(x: torch.Tensor, dest: torch.Tensor, M: int, mode: int = SCALE_EXACT, out=None):
+    """bf16 token rows [T, K] and int32 destinations [T, topk] (device) -> codes [M, K] and
+    scales [M, K/128] where row dest[t, k] (if in [0, M)) holds quant_act_1x128 of x[t].
+    Rows no destination names are left as they are: pass `out` when dest does not cover
+    all M rows (the outputs allocated here start uninitialized)."""
+    x = _bf16_payload(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [T, K]")
+    T, K = x.shape
+    if dest.dtype != torch.int32 or dest.dim() != 2 or dest.shape[0] != T or not dest.is_contiguous() or \
+            dest.device != x.device:
+        raise ValueError("dest must be a contiguous int32 [T, topk] tensor on x's device")
+    xq, xs = _pair_out(out, int(M), K, x.device)
+    _check("quant_act_1x128_scatter", lib().quant_act_1x128_scatter(_ptr(x), T, K, _ptr(dest), dest.shape[1], int(M),
+                                                                   _ptr(xq), _ptr(xs), int(mode), _stream(x)))
     return xq, xs
 
 

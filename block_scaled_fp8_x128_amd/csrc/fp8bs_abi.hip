@@ -185,6 +185,26 @@ int quant_act_1x128_gather(const void *x_bf16, int64_t T, int64_t K, const int32
         fp8bs::launch_quant_act_gather(x_bf16, T, K, rows, M, xq, xs, scale_mode, (hipStream_t)stream));
 }
 
+int quant_act_1x128_scatter(const void *x_bf16, int64_t T, int64_t K, const int32_t *dest, int64_t topk, int64_t M,
+                            void *xq, float *xs, int scale_mode, void *stream)
+{
+    if (T < 0 || M < 0 || K <= 0 || topk < 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))
+        return FP8BS_INVALID_ARG;
+    if (K % 128 != 0 || K >= kMaxDim || T >= kMaxDim || M >= kMaxDim || topk >= kMaxDim ||
+        T * (K / 128) >= kMaxDim || M * (K / 128) >= kMaxDim || T * topk >= kMaxDim)
+        return FP8BS_UNSUPPORTED_SHAPE;
+    if (T == 0 || topk == 0 || M == 0)
+        return FP8BS_OK;
+    if (!tensor_ok(x_bf16, T * K, 16) || !tensor_ok(dest, T * topk, 4) || !tensor_ok(xq, M * K, 16) ||
+        !tensor_ok(xs, M * K, 4))
+        return FP8BS_INVALID_ARG;
+    int st = check_device();
+    if (st != FP8BS_OK)
+        return st;
+    return status_of(
+        fp8bs::launch_quant_act_scatter(x_bf16, T, K, dest, topk, M, xq, xs, scale_mode, (hipStream_t)stream));
+}
+
 int swiglu_quant_1x128(const void *gu_bf16, int64_t M, int64_t F, void *hq, float *hs, int scale_mode, void *stream)
 {
     if (M < 0 || F <= 0 || (scale_mode != FP8BS_SCALE_EXACT && scale_mode != FP8BS_SCALE_POW2))
@@ -541,8 +561,9 @@ int fp8_kv_attention_decode(const void *q_bf16, const void *kq, const float *ks,
         return FP8BS_INVALID_ARG;
     if (!fp8bs::kv_attention_group_ok(Hq, Hkv))
         return FP8BS_UNSUPPORTED_SHAPE;
-    // 32-bit byte offsets within one sequence's cache rows; workgroup counts
-    if (T * Hkv * 128 >= kMaxDim || B * Hkv >= kMaxDim || B * Hq >= kMaxDim)
+    // 32-bit byte offsets within one sequence's cache rows (the kernel also
+    // forms those of one tile past the end); workgroup counts
+    if ((T + 128) * Hkv * 128 >= kMaxDim || B * Hkv >= kMaxDim || B * Hq >= kMaxDim)
         return FP8BS_UNSUPPORTED_SHAPE;
     if (B == 0)
         return FP8BS_OK;

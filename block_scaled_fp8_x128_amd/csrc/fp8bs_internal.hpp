@@ -40,6 +40,11 @@ hipError_t launch_quant_act_t(const void *x, int64_t M, int64_t K, void *xqt, fl
 // [0, T) reads as a zero row) (fp8bs_route.hip).
 hipError_t launch_quant_act_gather(const void *x, int64_t T, int64_t K, const int32_t *rows, int64_t M, void *xq,
                                    float *xs, int mode, hipStream_t stream);
+// The same dispatch from the token side: token row t (of x [T, K]) quantized
+// once, written to rows dest[t * topk + k] of xq [M, K], xs [M, K/128] that
+// lie in [0, M) (fp8bs_route.hip).
+hipError_t launch_quant_act_scatter(const void *x, int64_t T, int64_t K, const int32_t *dest, int64_t topk,
+                                    int64_t M, void *xq, float *xs, int mode, hipStream_t stream);
 // The gated activation of gu [M, 2F] (gate columns first), rounded to bf16,
 // then quantized 1x128: hq [M, F], hs [M, F/128] (fp8bs_swiglu.hip).
 hipError_t launch_swiglu_quant(const void *gu, int64_t M, int64_t F, void *hq, float *hs, int mode,

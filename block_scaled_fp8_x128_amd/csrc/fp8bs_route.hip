@@ -86,4 +86,74 @@ hipError_t launch_quant_act_gather(const void *x, int64_t T, int64_t K, const in
                   (const uint16_t *)x, T, rows, (u32x2 *)xq, xs, (uint32_t)nblocks, (uint32_t)(K / 128));
 }
 
+// The same dispatch from the token side: each token row is read once and
+// quantized once, and its codes and scales go to every destination row the
+// routing gives it:
+//
+//   for t < T, k < topk, d = dest[t * topk + k] in [0, M):  xq[d, :], xs[d, :] = quant_act_1x128(x[t, :])
+//
+// Reading each token once (instead of once per expert) leaves the codes'
+// writes as the main traffic.  Blocks are those of quant_act_1x128 over x
+// (one 16-lane DPP row per 1x128 block); the destinations of a block's token
+// are uniform over its DPP row, so every store is one block's 128 contiguous
+// code bytes.  Destinations outside [0, M) are skipped; rows no entry names
+// are not written.
+template <int MODE>
+__global__ __launch_bounds__(RG_THREADS) void quant_act_scatter_kernel(const uint16_t *__restrict__ x,
+                                                                     const int32_t *__restrict__ dest, int topk,
+                                                                     int64_t M, u32x2 *__restrict__ q,
+                                                                     float *__restrict__ s, uint32_t nblocks,
+                                                                     uint32_t KB)
+{
+    const int lane = threadIdx.x & 63;
+    const int slot = lane >> 4;
+    const int c = lane & 15;
+    const uint32_t wave = blockIdx.x * (RG_THREADS / 64) + (threadIdx.x >> 6);
+    const uint32_t b0 = wave * (4 * RG_UNROLL) + slot;
+
+    u32x4 v[RG_UNROLL];
+#pragma unroll
+    for (int j = 0; j < RG_UNROLL; ++j) {
+        const uint32_t b = b0 + 4 * j;
+        v[j] = (b < nblocks) ? __builtin_nontemporal_load((const u32x4 *)x + (int64_t)b * 16 + c)
+                             : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < RG_UNROLL; ++j) {
+        const uint32_t b = b0 + 4 * j;
+        // every lane takes part in the DPP reduction (blocks past the end hold zeros)
+        const float amax = amax_value(row16_max(chunk_max_mag(v[j])));
+        BlockQuant<MODE> bq;
+        bq.init(amax);
+        const u32x2 codes = quant_chunk<MODE>(v[j], bq);
+        if (b < nblocks) {
+            const uint32_t t = b / KB, kb = b - t * KB;
+            const int32_t *dt = dest + (int64_t)t * topk;
+            for (int k = 0; k < topk; ++k) {
+                const int64_t d = dt[k];
+                if (d >= 0 && d < M) {
+                    __builtin_nontemporal_store(codes, q + (d * KB + kb) * 16 + c);
+                    if (c == 0)
+                        s[d * KB + kb] = bq.s;
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_quant_act_scatter(const void *x, int64_t T, int64_t K, const int32_t *dest, int64_t topk,
+                                    int64_t M, void *xq, float *xs, int mode, hipStream_t stream)
+{
+    const int64_t nblocks = T * (K / 128);
+    if (nblocks == 0 || topk == 0)
+        return hipSuccess;
+    const int64_t grid = (nblocks + RG_BLOCKS_PER_WG - 1) / RG_BLOCKS_PER_WG;
+    if (mode == SCALE_POW2)
+        return launch(quant_act_scatter_kernel<SCALE_POW2>, dim3((unsigned)grid), dim3(RG_THREADS), 0, stream,
+                      (const uint16_t *)x, dest, (int)topk, M, (u32x2 *)xq, xs, (uint32_t)nblocks,
+                      (uint32_t)(K / 128));
+    return launch(quant_act_scatter_kernel<SCALE_EXACT>, dim3((unsigned)grid), dim3(RG_THREADS), 0, stream,
+                  (const uint16_t *)x, dest, (int)topk, M, (u32x2 *)xq, xs, (uint32_t)nblocks, (uint32_t)(K / 128));
+}
+
 } // namespace fp8bs

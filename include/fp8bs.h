@@ -152,6 +152,30 @@ FP8BS_API int quant_act_1x128_gather(const void *x_bf16, int64_t T, int64_t K, c
                                      void *xq, float *xs, int scale_mode, void *stream);
 
 /*
+ * quant_act_1x128_scatter -- the MoE dispatch from the token side: each token
+ * row is read and quantized once, and its codes and scales are written to
+ * every row the routing sends it to (the same result as quant_act_1x128_gather
+ * with the inverse map, with each token row read once instead of once per
+ * expert).
+ *
+ *   x_bf16 : [T, K] bf16 payloads (input): the token rows
+ *   dest   : [T, topk] int32 destination rows (device memory, never read by
+ *            the host): token t goes to rows dest[t * topk + k], k < topk
+ *   xq     : [M, K] E4M3 codes (output); xs : [M, K/128] fp32 scales (output)
+ *
+ * For every entry d = dest[t * topk + k] with 0 <= d < M: xq[d], xs[d] =
+ * quant_act_1x128(x[t]), bit for bit.  Entries outside [0, M) are skipped;
+ * rows that no entry names are not written.  Two entries naming the same row
+ * leave one of the two token rows there (which one is unspecified).  Errors:
+ * INVALID_ARG (negative sizes, bad scale_mode, null or misaligned x (16 B),
+ * dest (4 B), xq (16 B), xs (4 B) when T, topk and M are all positive),
+ * UNSUPPORTED_SHAPE (K % 128 != 0, a size or block count >= 2^31),
+ * UNSUPPORTED_DEVICE.  T, topk or M == 0 is a no-op.
+ */
+FP8BS_API int quant_act_1x128_scatter(const void *x_bf16, int64_t T, int64_t K, const int32_t *dest, int64_t topk,
+                                      int64_t M, void *xq, float *xs, int scale_mode, void *stream);
+
+/*
  * swiglu_quant_1x128 -- the MLP's gated activation fused with the 1x128
  * activation quantizer of the down projection's input.  The article keeps
  * non-linear functions in BF16 and runs the linear layers in FP8 (section

@@ -147,6 +147,19 @@ def moe_routing(tokens: int, experts: int, topk: int, seed: int = SEED,
     return row_token, offsets
 
 
+def moe_dest(row_token, tokens: int, topk: int) -> np.ndarray:
+    """The routing seen from the tokens: int32 [tokens, topk], entry (t, k) the row of the
+    expert-grouped matrix that holds token t's k-th copy (in row order), -1 where token t
+    has fewer than topk copies.  The inverse of ``row_token``."""
+    rt = np.asarray(row_token, dtype=np.int64)
+    dest = np.full((tokens, topk), -1, dtype=np.int32)
+    seen = np.zeros(tokens, dtype=np.int64)
+    for m, t in enumerate(rt):
+        dest[t, seen[t]] = m
+        seen[t] += 1
+    return dest
+
+
 def offsets_from_counts(counts) -> np.ndarray:
     """int32 group offsets (length E + 1) for explicit per-expert row counts."""
     c = np.asarray(counts, dtype=np.int64)
