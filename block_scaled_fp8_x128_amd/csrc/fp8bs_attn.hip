@@ -13,20 +13,27 @@
 //
 // Decode attention reads every cached byte once per step and does little
 // arithmetic per byte, so the cache bandwidth bounds it; FP8 halves those
-// bytes against bf16.  Work split: workgroup (b * Hkv + g, split) takes the
-// tokens [split * chunk, min((split + 1) * chunk, len_b)) of one key/value
-// head for all G = Hq / Hkv of its query heads; its 4 waves take 16-token
-// tiles in turn, each keeping its own running softmax (max, sum, output).
+// bytes against bf16.  Work split: workgroup (b * HG + hg, split) takes the
+// tokens [split * chunk, min((split + 1) * chunk, len_b)) of sequence b for
+// the key/value heads 8 hg .. 8 hg + 7, one per wave, each wave serving all
+// G = Hq / Hkv query heads of its key/value head and keeping their running
+// softmax (max, sum, output).  The cache rows are [T, Hkv, 128]: stepping
+// through 16-token tiles together, the waves of a workgroup read whole
+// contiguous token rows, where one head alone would take 128 bytes of every
+// Hkv * 128.
 //   scores: the tile's key codes become bf16 (exact: every E4M3 value is a
-//     bf16) and one v_mfma_f32_16x16x32_bf16 per 32 dimensions multiplies them
-//     by the query heads (bf16 products are exact in fp32); the key scale and
+//     bf16) and one v_mfma_f32_16x16x32_bf16 per 32 dimensions multiplies the
+//     query heads by them (bf16 products are exact in fp32), heads down the
+//     rows and tokens across the columns, so per-head max and sum over a tile
+//     are DPP reductions within a 16-lane row; the key scale and
 //     sm_scale * log2(e) follow in fp32, and exp2 replaces exp;
 //   values: each lane owns 8 dimensions of every fourth token of the tile and
 //     accumulates p * vs * decode(v) for the G heads in fp32, p coming from the
-//     scores through the wave's LDS area.
-// The waves' states merge through LDS; with several splits per sequence a
-// second kernel merges the splits' (max, sum, output) in split order.  Every
-// order is fixed, so results are deterministic.
+//     scores through the wave's LDS area; the four token groups' sums are
+//     added by two lane exchanges at the end.
+// With several splits per sequence a second kernel merges the splits' (max,
+// sum, output) in split order.  Every order is fixed, so results are
+// deterministic.
 #include "fp8bs_device.hpp"
 #include "fp8bs_internal.hpp"
 
@@ -37,7 +44,7 @@ typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 
 constexpr int AD = 128;       // head dimension (one 1x128 scale block)
-constexpr int ATT_WAVES = 4;
+constexpr int ATT_WAVES = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -50,7 +57,7 @@ struct AttnArgs {
     void *out;           // [B, Hq, 128]
     float *part;         // splits > 1: [B * Hq, splits, 2 + 128] (max, sum, output)
     int64_t B, T, Hq, Hkv;
-    int chunk;           // tokens per split (a multiple of 64)
+    int chunk;           // tokens per split (a multiple of 16)
     int splits;
     float scale_log2;    // sm_scale * log2(e)
 };
@@ -71,15 +78,44 @@ __device__ __forceinline__ bf8v codes_to_bf16(uint32_t w0, uint32_t w1)
     return bf8v{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Max and sum over the 16 lanes of a DPP row; every lane of the row gets the
+// result (the butterfly's partners: quad_perm [1,0,3,2], [2,3,0,1], then the
+// row's half mirror and full mirror).
+__device__ __forceinline__ float dpp_f(float v, int ctrl_id)
+{
+    const int x = __builtin_bit_cast(int, v);
+    int t;
+    switch (ctrl_id) {
+    case 0: t = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;
+    case 1: t = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;
+    case 2: t = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;
+    default: t = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float row16_fmax(float v)
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float t = dpp_f(v, c);
+        v = v > t ? v : t;
+    }
+    return v;
+}
+__device__ __forceinline__ float row16_fsum(float v)
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        v += dpp_f(v, c);
+    return v;
+}
+
 // LDS of one workgroup: per wave the tile's p * vs [16 tokens][G] and the
-// heads' rescale factors; then the waves' final states for the merge.
+// heads' rescale factors.
 template <int G>
 struct AttnLds {
     float pv[ATT_WAVES][16 * G];
     float alpha[ATT_WAVES][G];
-    float m[ATT_WAVES][G];
-    float l[ATT_WAVES][G];
-    float o[ATT_WAVES][G][AD];
 };
 
 template <int G, bool OUT_F32, bool SPLIT>
@@ -88,8 +124,10 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
     __shared__ AttnLds<G> sh;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t bg = blockIdx.x;
-    const int64_t b = bg / a.Hkv, g = bg % a.Hkv;
+    const int64_t HG = (a.Hkv + ATT_WAVES - 1) / ATT_WAVES; // groups of 8 key/value heads
+    const int64_t b = blockIdx.x / HG, g = (blockIdx.x % HG) * ATT_WAVES + wave;
+    if (g >= a.Hkv)
+        return; // (no barrier follows)
     const int split = blockIdx.y;
     int64_t len = a.lens[b];
     len = len < 0 ? 0 : (len > a.T ? a.T : len);
@@ -97,7 +135,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
     const int64_t t1 = (t0 + a.chunk) < len ? (t0 + a.chunk) : len;
     const int64_t rowb = a.Hkv * AD; // bytes between consecutive tokens of one head
 
-    // query fragments (MFMA B operand): lane (n = lane % 16, grp = lane / 16)
+    // query fragments (MFMA A operand): lane (n = lane % 16, grp = lane / 16)
     // holds the 8 dimensions 32 grp + 8 s .. + 7 of query head g G + n for
     // MFMA s (heads n >= G are zero); the key fragments below use the same
     // dimension order, so each MFMA s sums over its 32 dimensions once
@@ -116,8 +154,18 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
     const float *ksb = a.ks + (b * a.T) * a.Hkv + g;
     const float *vsb = a.vs + (b * a.T) * a.Hkv + g;
 
-    // the softmax state of head (lane % 16) (meaningful for heads < G) ...
-    float mh = -INFINITY, lh = 0.0f;
+    // Scores come out with heads down the MFMA's rows and the tile's 16
+    // tokens across its columns: lane (grp, n) holds heads 4 grp + r (r = 0
+    // .. 3) of token tb + n, so a head's max and sum over the tile are
+    // reductions within one 16-lane row (DPP), and each lane needs only its
+    // own token's scales.  The softmax state of head 4 grp + r is kept by
+    // every lane of its row (meaningful for heads < G) ...
+    float mh[4], lh[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        mh[r] = -INFINITY;
+        lh[r] = 0.0f;
+    }
     // ... and the output partials: lane (ts = lane / 16, c = lane % 16) sums
     // tokens ts, ts + 4, ts + 8, ts + 12 of each tile into dims 8 c .. 8 c + 7
     const int ts = grp, d0 = 8 * n;
@@ -128,69 +176,70 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
         for (int e = 0; e < 8; ++e)
             o[h][e] = 0.0f;
 
-    for (int64_t tb = t0 + 16 * wave; tb < t1; tb += 16 * ATT_WAVES) {
-        // ---- scores of tokens tb .. tb + 15 against the G heads ----
-        // A operand: lane (t = lane % 16, grp) holds bytes 32 grp .. + 31 of token tb + t
+    // The tile's operands, loaded one tile ahead: key bytes 32 grp .. + 31 of
+    // token tb + n (B operand of the score MFMAs) with that token's key and
+    // value scales, and value dims d0 .. d0 + 7 of tokens tb + ts + 4 u.  Loads
+    // past the sequence's length read zeros (buffer range check); the scales
+    // are read only below t1.
+    struct TileIn {
+        u32x4 k0, k1;
+        u32x2 v[4];
+        float ks, vs;
+    };
+    auto load_tile = [&](int64_t tb) {
+        TileIn in;
         const int koff = (int)((tb + n) * rowb) + 32 * grp;
-        const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 0, 0);
-        const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16, 0, 0);
-        // the tile's key and value scales: lane t < 16 loads token tb + t's
-        const bool tok_ok = n + tb < t1;
-        const float ksv = (lane < 16 && tok_ok) ? ksb[(tb + n) * a.Hkv] : 0.0f;
-        const float vsv = (lane < 16 && tok_ok) ? vsb[(tb + n) * a.Hkv] : 0.0f;
+        in.k0 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 0, 0);
+        in.k1 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            in.v[u] = __builtin_amdgcn_raw_buffer_load_b64(vr, (int)((tb + ts + 4 * u) * rowb) + d0, 0, 0);
+        const bool tok_ok = tb + n < t1;
+        in.ks = tok_ok ? ksb[(tb + n) * a.Hkv] : 0.0f;
+        in.vs = tok_ok ? vsb[(tb + n) * a.Hkv] : 0.0f;
+        return in;
+    };
+    TileIn nxt = load_tile(t0);
+    for (int64_t tb = t0; tb < t1; tb += 16) {
+        const TileIn cur = nxt;
+        // the next tile's loads go out before this tile's arithmetic
+        nxt = load_tile(tb + 16);
+        // ---- scores of the G heads against tokens tb .. tb + 15 ----
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(k0.x, k0.y), qf[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(k0.z, k0.w), qf[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(k1.x, k1.y), qf[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(k1.z, k1.w), qf[3], acc, 0, 0, 0);
-        // lane (grp, n) holds tokens tb + 4 grp + r of head n; scores in log2 units
-        float s[4], p[4];
-        float mt = -INFINITY;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[0], codes_to_bf16(cur.k0.x, cur.k0.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[1], codes_to_bf16(cur.k0.z, cur.k0.w), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[2], codes_to_bf16(cur.k1.x, cur.k1.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[3], codes_to_bf16(cur.k1.z, cur.k1.w), acc, 0, 0, 0);
+        const bool tok_ok = tb + n < t1;
+        const float kscale = cur.ks * a.scale_log2; // scores in log2 units
+        float p[4], alpha[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 4 * grp + r;
-            const float kscale = __shfl(ksv, t);
-            s[r] = (tb + t < t1) ? acc[r] * kscale * a.scale_log2 : -INFINITY;
-            mt = mt > s[r] ? mt : s[r];
+            const float s = tok_ok ? acc[r] * kscale : -INFINITY;
+            const float mt = row16_fmax(s);                       // finite: token tb is below t1
+            const float mnew = mh[r] > mt ? mh[r] : mt;
+            alpha[r] = __builtin_amdgcn_exp2f(mh[r] - mnew);      // 0 on the first tile
+            p[r] = __builtin_amdgcn_exp2f(s - mnew);              // 0 for masked tokens
+            lh[r] = lh[r] * alpha[r] + row16_fsum(p[r]);
+            mh[r] = mnew;
         }
-        float x = __shfl_xor(mt, 16);
-        mt = mt > x ? mt : x;
-        x = __shfl_xor(mt, 32);
-        mt = mt > x ? mt : x;
-        const float mnew = mh > mt ? mh : mt; // finite: the tile holds a token below t1
-        const float alpha = __builtin_amdgcn_exp2f(mh - mnew);
-        float ps = 0.0f;
+        // p * vs of each (token, head) and the heads' rescale factors to the wave's LDS
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(s[r] - mnew);
-            ps += p[r];
-        }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        lh = lh * alpha + ps;
-        mh = mnew;
-        // p * vs of each (token, head) and the heads' rescale factors to the
-        // wave's LDS (the shuffles run on every lane, outside the branch)
-        float vsr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            vsr[r] = __shfl(vsv, 4 * grp + r);
-        if (n < G) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sh.pv[wave][(4 * grp + r) * G + n] = p[r] * vsr[r];
-            if (grp == 0)
-                sh.alpha[wave][n] = alpha;
+            const int h = 4 * grp + r;
+            if (h < G) {
+                sh.pv[wave][n * G + h] = p[r] * cur.vs;
+                if (n == 0)
+                    sh.alpha[wave][h] = alpha[r];
+            }
         }
         // ---- values: tokens ts + 4 u of the tile, dims d0 .. d0 + 7 ----
         uint32_t vw[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int t = ts + 4 * u;
-            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, (int)((tb + t) * rowb) + d0, 0, 0);
-            const bool ok = tb + t < t1;
-            vw[u][0] = ok ? w.x : 0u;
-            vw[u][1] = ok ? w.y : 0u;
+            const bool ok = tb + ts + 4 * u < t1;
+            vw[u][0] = ok ? cur.v[u].x : 0u;
+            vw[u][1] = ok ? cur.v[u].y : 0u;
         }
         // (LDS writes and reads of one wave complete in order)
 #pragma unroll
@@ -220,7 +269,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
         }
     }
 
-    // ---- the wave's state: sum the four token groups' partials ----
+    // ---- sum the four token groups' partials; lanes of group 0 write ----
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -228,52 +277,44 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
             o[h][e] += __shfl_xor(o[h][e], 16);
             o[h][e] += __shfl_xor(o[h][e], 32);
         }
-    if (lane < G) {
-        sh.m[wave][lane] = mh;
-        sh.l[wave][lane] = lh;
+    // head h's (max, sum) sit in row h / 4, register h % 4, of every lane of that row
+    float mrow[G], lrow[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        mrow[h] = __shfl(mh[h % 4], 16 * (h / 4));
+        lrow[h] = __shfl(lh[h % 4], 16 * (h / 4));
     }
     if (grp == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+            const int64_t bh = b * a.Hq + g * G + h;
+            if constexpr (SPLIT) {
+                float *pp = a.part + (bh * a.splits + split) * (2 + AD);
+                if (n == 0) {
+                    pp[0] = mrow[h];
+                    pp[1] = lrow[h];
+                }
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sh.o[wave][h][d0 + e] = o[h][e];
-    }
-    __syncthreads();
-
-    // ---- merge the waves (in wave order): thread i handles dims of head i / 64 ... ----
-    for (int idx = threadIdx.x; idx < G * (AD / 2); idx += ATT_WAVES * 64) {
-        const int h = idx / (AD / 2), d = 2 * (idx % (AD / 2));
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < ATT_WAVES; ++w)
-            M = M > sh.m[w][h] ? M : sh.m[w][h];
-        float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < ATT_WAVES; ++w) {
-                const float f = __builtin_amdgcn_exp2f(sh.m[w][h] - M); // 0 for an empty wave
-                L = __builtin_fmaf(f, sh.l[w][h], L);
-                o0 = __builtin_fmaf(f, sh.o[w][h][d], o0);
-                o1 = __builtin_fmaf(f, sh.o[w][h][d + 1], o1);
-            }
-        }
-        const int64_t bh = b * a.Hq + g * G + h;
-        if constexpr (SPLIT) {
-            float *pp = a.part + (bh * a.splits + split) * (2 + AD);
-            if (d == 0) {
-                pp[0] = M;
-                pp[1] = L;
-            }
-            pp[2 + d] = o0;
-            pp[2 + d + 1] = o1;
-        } else {
-            const float r0 = L > 0.0f ? o0 / L : 0.0f, r1 = L > 0.0f ? o1 / L : 0.0f;
-            if constexpr (OUT_F32) {
-                *(f2v *)((float *)a.out + bh * AD + d) = f2v{r0, r1};
+                for (int e = 0; e < 8; ++e)
+                    pp[2 + d0 + e] = o[h][e];
             } else {
-                const bf2v v = __builtin_convertvector(f2v{r0, r1}, bf2v);
-                *(bf2v *)((__bf16 *)a.out + bh * AD + d) = v;
+                float r[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    r[e] = lrow[h] > 0.0f ? o[h][e] / lrow[h] : 0.0f;
+                if constexpr (OUT_F32) {
+                    float *op = (float *)a.out + bh * AD + d0;
+                    *(v4f *)op = v4f{r[0], r[1], r[2], r[3]};
+                    *(v4f *)(op + 4) = v4f{r[4], r[5], r[6], r[7]};
+                } else {
+                    const bf2v p0 = __builtin_convertvector(f2v{r[0], r[1]}, bf2v);
+                    const bf2v p1 = __builtin_convertvector(f2v{r[2], r[3]}, bf2v);
+                    const bf2v p2 = __builtin_convertvector(f2v{r[4], r[5]}, bf2v);
+                    const bf2v p3 = __builtin_convertvector(f2v{r[6], r[7]}, bf2v);
+                    *(u32x4 *)((__bf16 *)a.out + bh * AD + d0) =
+                        u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+                }
             }
         }
     }
@@ -308,20 +349,21 @@ __global__ __launch_bounds__(64) void kv_attn_combine_kernel(const float *part, 
     }
 }
 
-// Splits per sequence: enough workgroups to cover the CUs twice, each split at
-// least 256 tokens; the chunk is a multiple of the 4 waves' 16-token tiles.
+// Splits per sequence: enough workgroups (of up to 8 key/value heads each)
+// to give every CU two, each split at least 256 tokens; the chunk is a
+// multiple of the 16-token tile.
 static void attn_plan(int64_t B, int64_t T, int64_t Hkv, int &splits, int &chunk)
 {
-    const int64_t heads = B * Hkv;
-    int64_t s = (512 + heads - 1) / heads;
+    const int64_t groups = B * ((Hkv + ATT_WAVES - 1) / ATT_WAVES);
+    int64_t s = (512 + groups - 1) / groups;
     const int64_t smax = (T + 255) / 256;
     s = s < smax ? s : smax;
     s = s < 1 ? 1 : (s > 64 ? 64 : s);
     int64_t c = (T + s - 1) / s;
-    c = (c + 63) / 64 * 64;
+    c = (c + 15) / 16 * 16;
     s = (T + c - 1) / c;
     splits = (int)(s < 1 ? 1 : s);
-    chunk = (int)(c < 64 ? 64 : c);
+    chunk = (int)(c < 16 ? 16 : c);
 }
 
 size_t kv_attention_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv)
@@ -336,7 +378,8 @@ size_t kv_attention_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv
 template <int G>
 static hipError_t run_attn(const AttnArgs &a, bool out_f32, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)a.splits), block(ATT_WAVES * 64);
+    const dim3 grid((unsigned)(a.B * ((a.Hkv + ATT_WAVES - 1) / ATT_WAVES)), (unsigned)a.splits),
+        block(ATT_WAVES * 64);
     if (a.splits > 1) {
         hipError_t e = launch(kv_attn_decode_kernel<G, false, true>, grid, block, 0, stream, a);
         if (e != hipSuccess)
