@@ -699,12 +699,13 @@ def row_recal(fp8bs, dev, steps, warmup, cpu):
 def row_quant_act(fp8bs, dev, steps, warmup, cpu):
     """d2: the activation quantizer alone at the four activation shapes, each
     beside the runtime's device copy of the same byte count (half read, half
-    written); a 512 MiB write between launches keeps the inputs out of the
-    256 MB infinity cache."""
+    written); a 512 MiB read between launches keeps the inputs out of the
+    256 MB infinity cache (a write there would leave dirty lines whose
+    write-back the next launch would pay for)."""
     import synth
     import torch
     shapes = [(8192, 4096), (8192, 14336), (65536, 2048), (65536, 768)]
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     out = {"config": "quant_act_1x128 (EXACT) alone on [8192,4096] and [8192,14336] (8B dense layer inputs) and "
                      "[65536,2048] and [65536,768] (MoE gate+up and down inputs); cold inputs; "
                      "copy = torch copy_ of a uint8 buffer of half the algorithmic bytes"}
@@ -720,9 +721,9 @@ def row_quant_act(fp8bs, dev, steps, warmup, cpu):
         name = "%dx%d" % (M, K)
         for r in range(warmup + steps):
             t = timer if r >= warmup else None
-            scrub.fill_(r & 0xFF)
+            scrub.max()
             maybe(t, "quant_" + name, lambda: fp8bs.quant_act_1x128(x, 0, out=(xq, xs)))
-            scrub.fill_((r + 1) & 0xFF)
+            scrub.max()
             maybe(t, "copy_" + name, lambda: dst.copy_(src))
         torch.cuda.synchronize()
         tq, tc = timer.avg_ms("quant_" + name), timer.avg_ms("copy_" + name)
@@ -961,11 +962,11 @@ def row_attention(fp8bs, dev, steps, warmup, cpu):
     lens = torch.full((B,), T, dtype=torch.int32, device=dev)
     out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, fp8bs.kv_attention_workspace_size(B, T, Hq, Hkv)), dtype=torch.uint8, device=dev)
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     timer = KernelTimer()
     for r in range(warmup + steps):
         t = timer if r >= warmup else None
-        scrub.fill_(r & 0xFF)   # the 554 MB cache is larger than the 256 MB infinity cache anyway
+        scrub.max()   # (the 554 MB cache is larger than the 256 MB infinity cache anyway)
         maybe(t, "attn", lambda: fp8bs.fp8_kv_attention_decode(q, kq, ks, vq, vs, lens, 0.088388, out=out,
                                                                 workspace=ws))
     torch.cuda.synchronize()
