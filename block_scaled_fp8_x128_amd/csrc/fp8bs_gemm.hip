@@ -57,7 +57,10 @@ namespace fp8bs {
 
 constexpr int BK = 128;        // K block = scale block
 constexpr int NUM_XCD = 8;     // MI355X: 8 accelerator complex dies
-constexpr int GROUP_M = 8;
+// m-tiles per column sweep: the 32 units an XCD runs at once cover 4 m-tiles x 8
+// n-tiles (4 measured 0.6-1.1% faster than 8 over the four 8B-shaped GEMMs; 2
+// and 16 slower)
+constexpr int GROUP_M = 4;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct GemmCfg {
@@ -1399,7 +1402,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // and FP8BS_GEMM_KSPLIT=n the number of K ranges of the persistent dense
 // kernel; both are read once per process.
 
-enum Variant { V_AUTO = 0, V_SIMPLE = 1, V_DMA = 2, V_DMA8 = 3, V_SKINNY = 4 };
+enum Variant { V_AUTO = 0, V_SIMPLE = 1, V_DMA = 2, V_DMA8 = 3, V_SKINNY = 4, V_DMA64 = 5 };
 
 static int forced_variant()
 {
@@ -1415,6 +1418,8 @@ static int forced_variant()
             return (int)V_DMA8;
         if (!strcmp(e, "skinny"))
             return (int)V_SKINNY;
+        if (!strcmp(e, "dma64"))
+            return (int)V_DMA64;
         return (int)V_AUTO;
     }();
     return v;
@@ -1580,7 +1585,7 @@ static int choose_ksplit(int64_t tiles, int64_t KB)
     return best;
 }
 
-enum Kind { K_SIMPLE, K_DMA128, K_DMA256, K_SKINNY };
+enum Kind { K_SIMPLE, K_DMA128, K_DMA256, K_SKINNY, K_DMA64 };
 struct Plan {
     int kind;
     int tiles_m, tiles_n, ksplit;
@@ -1600,10 +1605,12 @@ static Plan plan_dense(int64_t M, int64_t N, int64_t K, bool row_scaled = false)
     }
     if (fv == V_SIMPLE || !dma_ok(N, K))
         return p;
-    // 256 x 256 tiles when they fill every CU at least once, else 128 x 256
+    // 256 x 256 tiles when they fill every CU at least once, else 128 x 256; at most 64 rows
+    // (decode): 64 x 256 tiles, which compute no padding rows at M = 64
     const bool big = fv == V_DMA8 || (fv != V_DMA && ((M + 255) / 256) * (N / 256) >= kPersistentGrid);
-    const int bm = big ? 256 : 128;
-    p.kind = big ? K_DMA256 : K_DMA128;
+    const bool rows64 = !big && !row_scaled && M <= 64 && (fv == V_AUTO || fv == V_DMA64);
+    const int bm = big ? 256 : (rows64 ? 64 : 128);
+    p.kind = big ? K_DMA256 : (rows64 ? K_DMA64 : K_DMA128);
     p.tiles_m = (int)((M + bm - 1) / bm);
     p.tiles_n = (int)(N / 256);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
@@ -1652,6 +1659,8 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
         return run_dma<256, 256, 4, 2, false>(a, out_fp32 != 0, pow2 != 0, stream);
     case K_DMA128:
         return run_dma<128, 256, 2, 4, false>(a, out_fp32 != 0, pow2 != 0, stream);
+    case K_DMA64:
+        return run_dma<64, 256, 1, 4, false>(a, out_fp32 != 0, pow2 != 0, stream);
     default:
         return run_simple<128, 128, 2, 2, false>(a, a.tiles_m * a.tiles_n, out_fp32 != 0, stream);
     }
