@@ -1605,10 +1605,13 @@ static Plan plan_dense(int64_t M, int64_t N, int64_t K, bool row_scaled = false)
     }
     if (fv == V_SIMPLE || !dma_ok(N, K))
         return p;
-    // 256 x 256 tiles when they fill every CU at least once, else 128 x 256; at most 64 rows
-    // (decode): 64 x 256 tiles, which compute no padding rows at M = 64
+    // 256 x 256 tiles when they fill every CU at least once, else 128 x 256; up to 128 rows
+    // (decode), 64 x 256 while those tiles fit in one round of workgroups: no padding rows at
+    // M = 64, and twice the units at M = 128
     const bool big = fv == V_DMA8 || (fv != V_DMA && ((M + 255) / 256) * (N / 256) >= kPersistentGrid);
-    const bool rows64 = !big && !row_scaled && M <= 64 && (fv == V_AUTO || fv == V_DMA64);
+    const bool rows64 =
+        !big && !row_scaled &&
+        ((fv == V_AUTO && M <= 128 && ((M + 63) / 64) * (N / 256) <= kPersistentGrid) || fv == V_DMA64);
     const int bm = big ? 256 : (rows64 ? 64 : 128);
     p.kind = big ? K_DMA256 : (rows64 ? K_DMA64 : K_DMA128);
     p.tiles_m = (int)((M + bm - 1) / bm);

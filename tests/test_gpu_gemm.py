@@ -56,6 +56,8 @@ SMALL = [
     # X-row chunks at M = 256), 16 / 32 / 64-row W tiles, K blocks not a multiple of the 8 waves
     (1, 256, 1024), (5, 512, 2048), (16, 1024, 1152), (24, 16384, 1024), (33, 512, 1024), (64, 2048, 1280),
     (100, 384, 2048), (256, 128, 1024), (7, 8192, 1024),
+    # 64-row persistent tiles up to 128 rows: ragged second row tile, and two full ones split along K
+    (100, 768, 2048), (128, 1024, 4096),
     # products split along K (fewer output tiles than compute units): 16 ranges of 4 blocks, uneven
     # ranges of 4 and 5 blocks (K/128 = 23), and 256-row tiles with a ragged second row tile
     (40, 512, 8192), (97, 512, 2944), (300, 512, 4096),
@@ -145,12 +147,12 @@ def test_gemm_empty(fp8bs):
     assert y.shape == (0, 128)
 
 
-# 8B-shaped dense layers (M = 8192) and the decode grid (M in {1, 16, 64, 256} against the
+# 8B-shaped dense layers (M = 8192) and the decode grid (M in {1, 16, 64, 128, 256} against the
 # gate+up and down weights), full size, every output
 LARGE = [
     ("qkv", 8192, 6144, 4096), ("gate_up", 8192, 28672, 4096), ("down", 8192, 4096, 14336),
     ("o_proj", 8192, 4096, 4096),
-] + [("decode%d_%s" % (m, name), m, n, k) for m in (1, 16, 64, 256)
+] + [("decode%d_%s" % (m, name), m, n, k) for m in (1, 16, 64, 128, 256)
      for name, n, k in (("gate_up", 28672, 4096), ("down", 4096, 14336))] + [
     # one K block per tile and more tiles than workgroups: every workgroup walks several one-step tiles
     ("k128_many_tiles", 4352, 4096, 128),
