@@ -1087,11 +1087,12 @@ def summarize_pmc(fetch_db, write_db, workload, command, out=None):
     return rec
 
 
-def summarize_trace(db, command, steps, warmup, out):
-    """Markdown summary of a rocprofv3 --kernel-trace database of `bench.py`: per kernel the
-    dispatch count and duration statistics, then the headline kernel's timed dispatches (the
-    dense layer's four GEMMs of steps warmup .. warmup + steps - 1, in dispatch order), the
-    figures the line's roofline divides by."""
+def summarize_trace(db, command, steps, warmup, out, workload="all"):
+    """Markdown summary of a rocprofv3 --kernel-trace database of `bench.py --workload
+    workload`: per kernel the dispatch count and duration statistics and, for the default run
+    and the dense workload, the headline kernel's timed dispatches (the dense layer's four
+    GEMMs of steps warmup .. warmup + steps - 1, in dispatch order), the figures the line's
+    roofline divides by."""
     import sqlite3
     c = sqlite3.connect(db)
     rows = c.execute("select s.display_name, d.start, d.end from rocpd_kernel_dispatch d join kernel_symbols s "
@@ -1101,7 +1102,8 @@ def summarize_trace(db, command, steps, warmup, out):
         per.setdefault(name, []).append((t1 - t0) / 1e3)
     srcs = ["block_scaled_fp8_x128_amd/csrc/" + f for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp8_x128_amd",
                                                                                       "csrc")))]
-    lines = ["# rocprofv3 kernel trace: `bench.py` default run", "",
+    title = "`bench.py` default run" if workload == "all" else "`bench.py --workload %s`" % workload
+    lines = ["# rocprofv3 kernel trace: " + title, "",
              "Command (on the MI355X box, from the repository root):", "", "    " + command, "",
              "Sources at the time of the trace (sha256, first 16 hex digits):", ""]
     lines += ["- `%s`: %s" % (f, src_hash(os.path.join(ROOT, f))) for f in srcs]
@@ -1109,7 +1111,7 @@ def summarize_trace(db, command, steps, warmup, out):
     dom = DOMINANT["dense"][0]
     heads = [d for (n, t0, t1), d in zip(rows, [(r[2] - r[1]) / 1e3 for r in rows])
              if n.startswith("void " + dom) or n.startswith(dom)]
-    first = heads[4 * warmup: 4 * (warmup + steps)]
+    first = heads[4 * warmup: 4 * (warmup + steps)] if workload in ("all", "dense") else []
     if first:
         srt = sorted(first)
         lines += ["## Headline kernel, timed dispatches", "",
@@ -1130,6 +1132,57 @@ def summarize_trace(db, command, steps, warmup, out):
     print("\n".join(lines[:40]))
 
 
+def summarize_counters(db, command, out):
+    """Markdown table of a rocprofv3 --pmc database of SQ / GRBM counters: per kernel the
+    dispatches, mean duration and the derived rates (where their counters were collected):
+    - clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration;
+    - MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8);
+    - VALU active = SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES;
+    - LDS indexed = SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES;
+    - wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES (waves stalled on a memory count or the barrier)."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    per = {}
+    for kname, cname, val, did, t0, t1 in c.execute("select kernel_name, counter_name, value, dispatch_id, start, end "
+                                                    "from counters_collection"):
+        d = per.setdefault(kname, {}).setdefault(did, {"dur_us": (t1 - t0) / 1e3})
+        d[cname] = d.get(cname, 0.0) + val
+    names = sorted({n for k in per.values() for d in k.values() for n in d if n != "dur_us"})
+
+    def mean(k, name):
+        v = [d[name] for d in per[k].values() if name in d]
+        return sum(v) / len(v) if v else None
+
+    def ratio(a, b, scale=1.0):
+        return None if a is None or not b else a / (b * scale)
+
+    lines = ["# rocprofv3 counters per kernel", "", "Command (on the MI355X box, from the repository root):", "",
+             "    " + command, "", "Counters: " + ", ".join("`%s`" % n for n in names), "",
+             "Sources at the time of the run (sha256, first 16 hex digits):", ""]
+    srcs = ["block_scaled_fp8_x128_amd/csrc/" + f for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp8_x128_amd",
+                                                                                      "csrc")))]
+    lines += ["- `%s`: %s" % (f, src_hash(os.path.join(ROOT, f))) for f in srcs + ["bench.py"]]
+    lines += ["", "| kernel | dispatches | mean us | clock MHz | MFMA busy | VALU active | LDS indexed | "
+                  "LDS bank conflicts | wait |", "|---|---|---|---|---|---|---|---|---|"]
+    order = sorted(per, key=lambda k: -sum(d["dur_us"] for d in per[k].values()))
+    fmt = lambda v, pct=True: "-" if v is None else ("%.1f%%" % (100 * v) if pct else "%.0f" % v)  # noqa: E731
+    for k in order[:12]:
+        dur = mean(k, "dur_us")
+        gui = mean(k, "GRBM_GUI_ACTIVE")
+        clock = None if gui is None or dur < 20 else gui / 8 / dur
+        mfma = ratio(mean(k, "SQ_VALU_MFMA_BUSY_CYCLES"), gui, 1024 / 8)
+        valu = ratio(mean(k, "SQ_ACTIVE_INST_VALU"), mean(k, "SQ_WAVE_CYCLES"))
+        lds = ratio(mean(k, "SQ_LDS_IDX_ACTIVE"), mean(k, "SQ_BUSY_CU_CYCLES"))
+        wait = ratio(mean(k, "SQ_WAIT_ANY"), mean(k, "SQ_WAVE_CYCLES"))
+        short = k.replace("void ", "").split("(")[0].replace("|", "/")
+        lines.append("| `%s` | %d | %.1f | %s | %s | %s | %s | %s | %s |" % (
+            short, len(per[k]), dur, fmt(clock, False), fmt(mfma), fmt(valu), fmt(lds),
+            fmt(mean(k, "SQ_LDS_BANK_CONFLICT"), False), fmt(wait)))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
@@ -1146,13 +1199,19 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     ap.add_argument("--pmc-command", default="", help="the profiled command, recorded with --summarize-pmc")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DB", "OUT_MD"),
-                    help="summarize a rocprofv3 --kernel-trace database of this script's default run")
+                    help="summarize a rocprofv3 --kernel-trace database of this script (with --workload)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DB", "OUT_MD"),
+                    help="summarize a rocprofv3 --pmc database of SQ / GRBM counters")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.pmc_command, args.summarize_counters[1])
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.pmc_command, args.steps, args.warmup, args.summarize_trace[1])
+        summarize_trace(args.summarize_trace[0], args.pmc_command, args.steps, args.warmup, args.summarize_trace[1],
+                        args.workload)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
