@@ -444,6 +444,25 @@ def decode_workload(fp8bs, dev, mode):
                 maybe(timer, "gemm_" + p["name"],
                       lambda p=p, wq=wq, ws=ws: gemm(p["xq"], p["xs"], wq, ws, out=p["y"], workspace=p["ws_buf"]))
 
+    def stream(timer, reps):
+        # five back-to-back calls of one pair per event pair, one per weight copy (each copy last read
+        # four calls, 235 MB or more of weights, earlier): the per-launch time without each launch's
+        # own start-up, as in a decode step that runs its layers back to back
+        for r in range(reps):
+            for p in pairs:
+                def gemms(p=p):
+                    for c in range(5):
+                        wq, ws = p["copies"][(r + p["j"] + 1 + c) % 5]
+                        gemm(p["xq"], p["xs"], wq, ws, out=p["y"], workspace=p["ws_buf"])
+
+                def linears(p=p):
+                    for c in range(5):
+                        wq, ws = p["copies"][(r + p["j"] + 1 + c) % 5]
+                        linear(p["x"], wq, ws, out=p["y"], workspace=p["lin_buf"])
+                maybe(timer, "gemm5_" + p["name"], gemms)
+                maybe(timer, "linear5_" + p["name"], linears)
+
+    step.stream = stream
     flops = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pairs)
     return step, separate, pairs, flops
 
@@ -699,40 +718,67 @@ def row_recal(fp8bs, dev, steps, warmup, cpu):
 def row_quant_act(fp8bs, dev, steps, warmup, cpu):
     """d2: the activation quantizer alone at the four activation shapes, each
     beside the runtime's device copy of the same byte count (half read, half
-    written); a 512 MiB read between launches keeps the inputs out of the
-    256 MB infinity cache (a write there would leave dirty lines whose
-    write-back the next launch would pay for)."""
+    written).  Timed two ways:
+    - single: one launch between two events, after a 512 MiB read that keeps
+      the input out of the 256 MB infinity cache (a write there would leave
+      dirty lines whose write-back the next launch would pay for); the events
+      also count the launch's own start-up;
+    - stream (the roofline figure): R back-to-back launches between two
+      events, each on its own input and output copy, R copies holding more
+      than 600 MB, so that every launch reads an input last touched more than
+      500 MB of traffic earlier (out of the cache) and the launches' start-up
+      overlaps the previous launch, as in a layer step."""
     import synth
     import torch
     shapes = [(8192, 4096), (8192, 14336), (65536, 2048), (65536, 768)]
     scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     out = {"config": "quant_act_1x128 (EXACT) alone on [8192,4096] and [8192,14336] (8B dense layer inputs) and "
-                     "[65536,2048] and [65536,768] (MoE gate+up and down inputs); cold inputs; "
-                     "copy = torch copy_ of a uint8 buffer of half the algorithmic bytes"}
+                     "[65536,2048] and [65536,768] (MoE gate+up and down inputs); cold inputs; stream = R "
+                     "back-to-back launches on R rotated input/output copies (> 600 MB) per event pair, single = "
+                     "one launch per event pair after a cache-evicting read; copy = torch copy_ of a uint8 "
+                     "buffer of half the algorithmic bytes, timed the same two ways"}
     timer = KernelTimer()
     for i, (M, K) in enumerate(shapes):
-        x = synth.activations_dev(M, K, dev, sub=synth.SUB_X + 50 + i)
-        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-        xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
         nbytes = M * K * ACT_BPE
+        R = max(2, int(-(-600e6 // nbytes)))
+        x0 = synth.activations_dev(M, K, dev, sub=synth.SUB_X + 50 + i)
+        xs_in = [x0] + [x0.clone() for _ in range(R - 1)]
+        outs = [(torch.empty((M, K), dtype=torch.uint8, device=dev),
+                 torch.empty((M, K // 128), dtype=torch.float32, device=dev)) for _ in range(R)]
         half = int(nbytes // 2) // 16 * 16
-        src = torch.empty(half, dtype=torch.uint8, device=dev)
-        dst = torch.empty(half, dtype=torch.uint8, device=dev)
+        srcs = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(R)]
+        dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(R)]
         name = "%dx%d" % (M, K)
+
+        # (copies 1 .. R - 1, then 0: the single launch just read copy 0)
+        order = list(range(1, R)) + [0]
+
+        def quant_burst():
+            for c in order:
+                fp8bs.quant_act_1x128(xs_in[c], 0, out=outs[c])
+
+        def copy_burst():
+            for c in order:
+                dsts[c].copy_(srcs[c])
         for r in range(warmup + steps):
             t = timer if r >= warmup else None
             scrub.max()
-            maybe(t, "quant_" + name, lambda: fp8bs.quant_act_1x128(x, 0, out=(xq, xs)))
+            maybe(t, "quant1_" + name, lambda: fp8bs.quant_act_1x128(xs_in[0], 0, out=outs[0]))
             scrub.max()
-            maybe(t, "copy_" + name, lambda: dst.copy_(src))
+            maybe(t, "copy1_" + name, lambda: dsts[0].copy_(srcs[0]))
+            maybe(t, "quantR_" + name, quant_burst)
+            maybe(t, "copyR_" + name, copy_burst)
         torch.cuda.synchronize()
-        tq, tc = timer.avg_ms("quant_" + name), timer.avg_ms("copy_" + name)
-        med, mn = timer.spread("quant_" + name)
-        out[name] = {**hbm_entry(tq, nbytes), "median_ms": round(med, 4), "min_ms": round(mn, 4),
-                     "copy_ms": round(tc, 4), "copy_GB/s": round(2 * half / (tc * 1e-3) / 1e9, 1),
+        tq, tc = timer.avg_ms("quantR_" + name) / R, timer.avg_ms("copyR_" + name) / R
+        t1q, t1c = timer.avg_ms("quant1_" + name), timer.avg_ms("copy1_" + name)
+        med, mn = timer.spread("quantR_" + name)
+        out[name] = {**hbm_entry(tq, nbytes), "median_ms": round(med / R, 4), "min_ms": round(mn / R, 4),
+                     "copies": R, "copy_ms": round(tc, 4), "copy_GB/s": round(2 * half / (tc * 1e-3) / 1e9, 1),
                      "frac_of_copy": round(tc / tq, 4),
+                     "single": {**hbm_entry(t1q, nbytes), "copy_ms": round(t1c, 4)},
                      "roofline": roof_hbm("fp8bs::quant_act_kernel", tq, nbytes)}
-        del x, xq, xs, src, dst
+        del x0, xs_in, outs, srcs, dsts
+        torch.cuda.empty_cache()
     del scrub
     torch.cuda.empty_cache()
     if cpu:
@@ -779,13 +825,18 @@ def row_decode(fp8bs, dev, steps, warmup, cpu):
     ms = timed_loop(step, steps, warmup, timer)
     separate(None, 2)
     separate(timer, steps)
+    step.stream(None, 1)
+    step.stream(timer, steps)
     import torch
     torch.cuda.synchronize()
     out = {"config": "M in {1,16,64,256} x (gate+up K4096 N28672, down K14336 N4096), EXACT; linear = "
-                     "fp8_block_linear from bf16 X (one launch for M <= 16), gemm = fp8_block_gemm alone",
+                     "fp8_block_linear from bf16 X (one launch for M <= 16), gemm = fp8_block_gemm alone; "
+                     "per call: one call per event pair (its own start-up included); roofline: five calls "
+                     "back to back per event pair, one per rotated weight copy",
            "ms_per_step": round(ms, 4)}
     for p in pairs:
         tl, tg = timer.avg_ms("linear_" + p["name"]), timer.avg_ms("gemm_" + p["name"])
+        tl5, tg5 = timer.avg_ms("linear5_" + p["name"]) / 5, timer.avg_ms("gemm5_" + p["name"]) / 5
         wb = p["N"] * p["K"] * (1 + 4 / 16384) + p["M"] * p["N"] * 2
         gbytes = wb + p["M"] * p["K"] * (1 + 4 / 128)
         lbytes = wb + p["M"] * p["K"] * 2
@@ -793,11 +844,13 @@ def row_decode(fp8bs, dev, steps, warmup, cpu):
         lm, lmin = timer.spread("linear_" + p["name"])
         gm, gmin = timer.spread("gemm_" + p["name"])
         out[p["name"]] = {
-            "linear": {**hbm_entry(tl, lbytes), "median_ms": round(lm, 4), "min_ms": round(lmin, 4),
+            "linear": {**hbm_entry(tl5, lbytes), "per_call_ms": round(tl, 4), "per_call_median_ms": round(lm, 4),
+                       "per_call_min_ms": round(lmin, 4),
                        "fused": fp8bs.linear_workspace_size(p["M"], p["N"], p["K"]) == 0,
-                       "roofline": roof_hbm("fp8_block_linear", tl, lbytes)},
-            "gemm": {**hbm_entry(tg, gbytes), "median_ms": round(gm, 4), "min_ms": round(gmin, 4),
-                     "roofline": roof_binding("fp8_block_gemm", tg, fl, gbytes)}}
+                       "roofline": roof_hbm("fp8_block_linear", tl5, lbytes)},
+            "gemm": {**hbm_entry(tg5, gbytes), "per_call_ms": round(tg, 4), "per_call_median_ms": round(gm, 4),
+                     "per_call_min_ms": round(gmin, 4),
+                     "roofline": roof_binding("fp8_block_gemm", tg5, fl, gbytes)}}
     del pairs
     torch.cuda.empty_cache()
     if cpu:
@@ -1308,6 +1361,8 @@ def main():
         ms = timed_loop(step, args.steps, args.warmup, timer)
         separate(None, 2)
         separate(timer, args.steps)
+        step.stream(None, 1)
+        step.stream(timer, args.steps)
         torch.cuda.synchronize()
         kernels = {}
         for p in pairs:
@@ -1322,9 +1377,11 @@ def main():
                                               "fused": fp8bs.linear_workspace_size(p["M"], p["N"], p["K"]) == 0}
             kernels["gemm_" + p["name"]] = {**hbm_entry(tg, gbytes), "TFLOP/s": tf(tg)}
             kernels["quant_plus_gemm_" + p["name"]] = hbm_entry(tq + tg, gbytes + p["M"] * p["K"] * 2)
-        # the step's longest single GEMM launch: the largest M (persistent kernel split along K)
+            kernels["gemm_stream_" + p["name"]] = hbm_entry(timer.avg_ms("gemm5_" + p["name"]) / 5, gbytes)
+        # the step's longest GEMM: gate+up at the largest M (the persistent 128x256 kernel), timed as
+        # five back-to-back launches on rotated weight copies
         big = max(pairs, key=lambda p: p["N"] * p["K"] + p["M"])
-        tb = timer.avg_ms("gemm_" + big["name"])
+        tb = timer.avg_ms("gemm5_" + big["name"]) / 5
         nb = big["N"] * big["K"] * (1 + 4 / 16384) + big["M"] * big["K"] * (1 + 4 / 128) + big["M"] * big["N"] * 2
         ach = nb / (tb * 1e-3) / 1e9
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", **common,
@@ -1332,7 +1389,7 @@ def main():
                "config": {"workload": "rollout decode: M in {1,16,64,256} x (gate+up K4096 N28672, down K14336 "
                                       "N4096), fp8_block_linear from bf16 activations (quantized inside the GEMM "
                                       "for M <= 16), 5 rotated weight copies"},
-               "roofline": {"kernel": "fp8_block_gemm (persistent 128x256 kernel split along K), %s" % big["name"],
+               "roofline": {"kernel": "fp8_block_gemm (persistent 128x256 kernel), %s" % big["name"],
                             "bound": "hbm",
                             "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None},
