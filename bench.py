@@ -76,7 +76,7 @@ COPY_BYTES = 1 << 30
 DOMINANT = {
     "dense": ("fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, false, 0>", GEMM_SRC,
               "gemm_dma_256x256_dense_m8192_traffic.json"),
-    "recal": ("fp8bs::quant_w_kernel<0>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
+    "recal": ("fp8bs::quant_w_kernel<0, 4>", QUANT_SRC, "quant_w_recal_32layers_traffic.json"),
     # the grouped gate+up call: its row-tile table, the 256-row pass and the short-tile pass
     "moe": ("fp8_block_grouped_gemm gate+up", GEMM_SRC, "grouped_gemm_moe_gate_up_traffic.json"),
 }
@@ -706,7 +706,7 @@ def row_recal(fp8bs, dev, steps, warmup, cpu):
            "ms_per_step": round(ms, 4), "bytes_per_pass": nbytes}
     for mode, name in ((0, "exact"), (1, "pow2")):
         t = timer.avg_ms("recal_" + name)
-        out[name] = {**hbm_entry(t, nbytes), "roofline": roof_hbm(DOMINANT["recal"][0].replace("<0>", "<%d>" % mode)
+        out[name] = {**hbm_entry(t, nbytes), "roofline": roof_hbm(DOMINANT["recal"][0].replace("<0,", "<%d," % mode)
                                                                   + " (batched)", t, nbytes,
                                                                   *((traffic, tsrc) if mode == 0 else (None, None)))}
     with_spread({"recal_exact": out["exact"], "recal_pow2": out["pow2"]}, timer)
