@@ -83,8 +83,8 @@ hipError_t launch_quant_act(const void *x, int64_t M, int64_t K, void *xq, float
 // ---- weights: 128x128 blocks -----------------------------------------------------
 //
 // A workgroup of 256 BW threads quantizes BW horizontally adjacent 128x128
-// blocks of one 128-row band (BW = 4 where every tensor of the launch has a
-// multiple of 4 K blocks, else 2, else 1).  Lane l of a wave reads the 16-byte
+// blocks of one 128-row band (BW = 4 for a tensor with a multiple of 4 K
+// blocks, else 2 for a multiple of 2, else 1).  Lane l of a wave reads the 16-byte
 // chunk l % (16 BW) of row l / (16 BW) of a group of rows, so one load
 // instruction covers 256 BW contiguous bytes of each of 4 / BW rows; thread t
 // covers its row and the rows 16, 32, ..., 112 below it: eight loads in flight
@@ -200,22 +200,26 @@ static hipError_t launch_quant_w_bw(const WTensor *t, int64_t n, int mode, hipSt
     return launch(quant_w_kernel<SCALE_EXACT, BW>, dim3((unsigned)tiles), dim3(QW_THREADS * BW), 0, stream, a);
 }
 
+// Each tensor goes to the widest band that divides its K blocks: one launch
+// per band width present, each over up to QW_MAX_TENSORS tensors.
 hipError_t launch_quant_w(const WTensor *t, int64_t count, int mode, hipStream_t stream)
 {
-    for (int64_t first = 0; first < count; first += QW_MAX_TENSORS) {
-        const int64_t n = (count - first) < QW_MAX_TENSORS ? (count - first) : QW_MAX_TENSORS;
-        // the widest band that divides every tensor's K blocks
-        bool by4 = true, by2 = true;
-        for (int64_t j = 0; j < n; ++j) {
-            const int64_t kb = t[first + j].K / 128;
-            by4 = by4 && kb % 4 == 0;
-            by2 = by2 && kb % 2 == 0;
+    WTensor part[QW_MAX_TENSORS];
+    for (int bw = 4; bw >= 1; bw /= 2) {
+        int64_t n = 0;
+        for (int64_t j = 0; j <= count; ++j) {
+            const bool take = j < count && (t[j].K / 128) % bw == 0 && (bw == 4 || (t[j].K / 128) % (2 * bw) != 0);
+            if (take)
+                part[n++] = t[j];
+            if (n == QW_MAX_TENSORS || (j == count && n > 0)) {
+                const hipError_t e = bw == 4   ? launch_quant_w_bw<4>(part, n, mode, stream)
+                                     : bw == 2 ? launch_quant_w_bw<2>(part, n, mode, stream)
+                                               : launch_quant_w_bw<1>(part, n, mode, stream);
+                if (e != hipSuccess)
+                    return e;
+                n = 0;
+            }
         }
-        const hipError_t e = by4   ? launch_quant_w_bw<4>(t + first, n, mode, stream)
-                             : by2 ? launch_quant_w_bw<2>(t + first, n, mode, stream)
-                                   : launch_quant_w_bw<1>(t + first, n, mode, stream);
-        if (e != hipSuccess)
-            return e;
     }
     return hipSuccess;
 }
