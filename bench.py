@@ -220,6 +220,7 @@ def dense_workload(fp8bs, dev, mode):
 def train_workload(fp8bs, dev, mode):
     """Backward data gradients of the same four layers: dX [M, K] = dY [M, N] W [N, K]."""
     gemm = fp8bs.fp8_block_gemm_pow2 if mode else fp8bs.fp8_block_gemm
+    wgrad = fp8bs.fp8_block_gemm_1x128_pow2 if mode else fp8bs.fp8_block_gemm_1x128
     import synth
     import torch
     M = 8192
@@ -260,18 +261,22 @@ def train_workload(fp8bs, dev, mode):
                   lambda: gemm(b["dyq"], b["dys"], b["outs"][2], b["outs"][3], out=b["dx"]))
             maybe(timer, "quant_act_t_x_" + b["name"], lambda: fp8bs.quant_act_1x128_t(b["x"], mode, out=b["xt"]))
             maybe(timer, "wgrad_" + b["name"],
-                  lambda: fp8bs.fp8_block_gemm_1x128(b["dyt"][0], b["dyt"][1], b["xt"][0], b["xt"][1], out=b["dw"]))
+                  lambda: wgrad(b["dyt"][0], b["dyt"][1], b["xt"][0], b["xt"][1], out=b["dw"]))
 
     # data and weight gradients: twice the forward FLOPs
     flops = sum(4.0 * b["M"] * b["N"] * b["K"] for b in bufs)
     return step, bufs, flops
 
 
-def summarize_train(bufs, timer):
+def summarize_train(bufs, timer, mode=0):
     """The data-gradient half as summarize_dense, plus the weight-gradient GEMMs and
     the transposing quantizers; the roofline object covers whichever GEMM kernel
-    takes more of the step."""
+    takes more of the step (with POW2 scales: the kernels that take them on the
+    matrix cores)."""
     kernels, roof = summarize_dense(bufs, timer, dual=True)
+    if mode:
+        roof["kernel"] = roof["kernel"].replace("false, false, false, false, false, 0>",
+                                                "false, false, false, true, false, 0>")
     w_ms, w_flops = [], []
     for b in bufs:
         M, N, K = b["M"], b["N"], b["K"]   # (tokens, forward K, forward N)
@@ -288,8 +293,9 @@ def summarize_train(bufs, timer):
     if sum(w_ms) > d_ms:
         mean_ms, mean_flops = sum(w_ms) / len(w_ms), sum(w_flops) / len(w_flops)
         ach = mean_flops / (mean_ms * 1e-3) / 1e12
-        roof = {"kernel": "fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, false, true, 0> (weight "
-                          "gradients of QKV, gate+up, down, o_proj over 8192 tokens)", "bound": "mfma",
+        roof = {"kernel": "fp8bs::gemm_dma_kernel<256, 256, 4, 2, false, false, false, %s, true, 0> (weight "
+                          "gradients of QKV, gate+up, down, o_proj over 8192 tokens)" % ("true" if mode else "false"),
+                "bound": "mfma",
                 "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": None,
                 "algorithmic_flop_per_launch": mean_flops, "avg_launch_ms": round(mean_ms, 4),
@@ -1328,7 +1334,7 @@ def main():
     elif args.workload == "train":
         step, bufs, flops = train_workload(fp8bs, dev, args.mode)
         ms = timed_loop(step, args.steps, args.warmup, timer)
-        kernels, roof = summarize_train(bufs, timer)
+        kernels, roof = summarize_train(bufs, timer, args.mode)
         out = {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", **common,
                "ms_per_step": round(ms, 4), "dtype": "fp8e4m3",
                "config": {"workload": "training backward of the 8B-shaped dense layer at M=8192 tokens: "

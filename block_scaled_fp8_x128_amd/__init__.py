@@ -46,6 +46,7 @@ EXPORTS = (
     "quant_w_128x128_dual_batched",
     "fp8_block_gemm",
     "fp8_block_gemm_1x128",
+    "fp8_block_gemm_1x128_pow2",
     "fp8_block_grouped_gemm",
     "fp8_block_gemm_pow2",
     "fp8_block_grouped_gemm_pow2",
@@ -87,6 +88,7 @@ def lib() -> ctypes.CDLL:
         L.quant_act_1x128_gather.argtypes = [P, I64, I64, P, I64, P, P, I32, P]
         L.quant_act_1x128_scatter.argtypes = [P, I64, I64, P, I64, I64, P, P, I32, P]
         L.fp8_block_gemm_1x128.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+        L.fp8_block_gemm_1x128_pow2.argtypes = L.fp8_block_gemm_1x128.argtypes
         L.quant_w_128x128.argtypes = [P, I64, I64, P, P, I32, P]
         L.quant_w_128x128_batched.argtypes = [I64, P, P, P, P, P, I32, P]
         L.quant_w_128x128_dual.argtypes = [P, I64, I64, P, P, P, P, I32, P]
@@ -115,7 +117,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bs_abi_version.restype = I32
         for fn in ("quant_act_1x128", "quant_act_1x128_t", "quant_act_1x128_dual", "swiglu_quant_1x128",
                    "quant_act_1x128_gather", "quant_act_1x128_scatter",
-                   "fp8_block_gemm_1x128", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
+                   "fp8_block_gemm_1x128", "fp8_block_gemm_1x128_pow2", "quant_w_128x128", "quant_w_128x128_batched", "quant_w_128x128_dual",
                    "quant_w_128x128_dual_batched", "fp8_block_gemm",
                    "fp8_block_grouped_gemm", "fp8_block_gemm_pow2", "fp8_block_grouped_gemm_pow2",
                    "fp8_block_grouped_gemm_noalloc", "fp8_block_gemm_quant", "fp8_kv_attention_decode",
@@ -441,6 +443,16 @@ def fp8_block_gemm_pow2(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None, work
 def fp8_block_gemm_1x128(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None):
     """Y [M, N] with 1x128 scales on both operands (ws [N, K/128]): the weight gradient
     dW = dY^T X from quant_act_1x128_t(dY) and quant_act_1x128_t(X)."""
+    return _gemm_1x128("fp8_block_gemm_1x128", xq, xs, wq, ws, out_dtype, out)
+
+
+def fp8_block_gemm_1x128_pow2(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None):
+    """fp8_block_gemm_1x128 for operands quantized with power-of-2 scales (both scales go to the
+    matrix cores)."""
+    return _gemm_1x128("fp8_block_gemm_1x128_pow2", xq, xs, wq, ws, out_dtype, out)
+
+
+def _gemm_1x128(fn, xq, xs, wq, ws, out_dtype, out):
     xq, wq = _codes(xq, "xq"), _codes(wq, "wq")
     xs, ws = _f32(xs, "xs"), _f32(ws, "ws")
     M, K = xq.shape
@@ -450,8 +462,7 @@ def fp8_block_gemm_1x128(xq, xs, wq, ws, out_dtype=torch.bfloat16, out=None):
     _same_device(xq.device, ("xs", xs), ("wq", wq), ("ws", ws))
     code = _out_code(out_dtype)
     out = _y_out(out, M, N, code, xq.device)
-    _check("fp8_block_gemm_1x128", lib().fp8_block_gemm_1x128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
-                                                              _ptr(out), code, _stream(xq)))
+    _check(fn, getattr(lib(), fn)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(out), code, _stream(xq)))
     return out
 
 

@@ -328,8 +328,8 @@ int quant_w_128x128_dual_batched(int64_t count, const void *const *w_bf16, const
     return quant_w_dual_impl(count, w_bf16, N, K, wq, ws, wqt, wst, scale_mode, stream);
 }
 
-int fp8_block_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
-                         int64_t K, void *y, int out_dtype, void *stream)
+static int gemm_1x128_impl(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                           int64_t K, void *y, int out_dtype, int pow2, void *stream)
 {
     int st = check_gemm_common(xq, xs, y, M, N, K, out_dtype);
     if (st != FP8BS_OK)
@@ -341,8 +341,20 @@ int fp8_block_gemm_1x128(const void *xq, const float *xs, const void *wq, const 
         return FP8BS_OK;
     if ((st = check_device()) != FP8BS_OK)
         return st;
-    return status_of(fp8bs::launch_gemm_1x128(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32,
+    return status_of(fp8bs::launch_gemm_1x128(xq, xs, wq, ws, M, N, K, y, out_dtype == FP8BS_OUT_FP32, pow2,
                                               (hipStream_t)stream));
+}
+
+int fp8_block_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                         int64_t K, void *y, int out_dtype, void *stream)
+{
+    return gemm_1x128_impl(xq, xs, wq, ws, M, N, K, y, out_dtype, 0, stream);
+}
+
+int fp8_block_gemm_1x128_pow2(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
+                              int64_t K, void *y, int out_dtype, void *stream)
+{
+    return gemm_1x128_impl(xq, xs, wq, ws, M, N, K, y, out_dtype, 1, stream);
 }
 
 size_t fp8bs_gemm_workspace_size(int64_t M, int64_t N, int64_t K)

@@ -609,7 +609,9 @@ __device__ __forceinline__ bool tile_geo(const GemmArgs &a, int v, int nunits, T
 // WROW: per-row weight scales ws [N, K/128] (the weight gradient, whose both
 // operands are quantized in 1x128 blocks along the tokens): each K step's BN
 // W-row scales travel with its operands into a ring of LDS slots, and the
-// rescale forms xs * ws for each lane's 4 columns of a tile.
+// rescale forms xs * ws for each lane's 4 columns of a tile; with POW2 each
+// lane instead passes the scale of the W row it holds to the MFMA's E8M0
+// operand of the weight operand, and both scales reach the matrix core.
 // QMODE (1 = EXACT, 2 = POW2 scales): the bf16 output is also quantized in
 // 1x128 blocks along its rows, as quant_act_1x128 would quantize it, for a
 // next layer that takes FP8 input: codes to a.yq [M, N], scales to a.ys
@@ -618,7 +620,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, bool OUT_F32, bool GROUPED, 
           bool WROW = false, int QMODE = 0>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArgs args)
 {
-    static_assert(!(WROW && (POW2 || GROUPED)), "per-row weight scales: dense products, VALU rescale");
+    static_assert(!(WROW && GROUPED), "per-row weight scales: dense products");
     static_assert(QMODE == 0 || (!OUT_F32 && !SPLIT && !WROW && !GROUPED && BN / WAVES_N == 128),
                   "the quantizing epilogue: bf16 output, whole K, one 128-column block per wave");
     GemmArgs a = args;
@@ -828,6 +830,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         const uint8_t *L = lds + stage * C::STAGE_BYTES;
         const uint8_t *Ln = lds + nstage * C::STAGE_BYTES;
         const uint8_t *Lw = lds + C::WSR_OFF + wcur * C::WSR_STRIDE + (wn * C::WN + 4 * fg) * 4;
+        // (POW2 with per-row weight scales: the scale of W row fr of each 16-row tile, this lane's
+        // row of the MFMA's weight operand)
+        const uint8_t *Lwe = lds + C::WSR_OFF + wcur * C::WSR_STRIDE + (wn * C::WN + fr) * 4;
         v4f part[2];
         float xs_next[C::TM];
         float sw_next = 0.f;
@@ -850,7 +855,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             const bool last = j + 1 == C::TN;
             // (issued before the group's fragment reads: LDS reads complete in
             // order, so waiting for it leaves those in flight)
-            if constexpr (WROW)
+            int e8wj = e8w;
+            if constexpr (WROW && POW2)
+                e8wj = (int)(__builtin_bit_cast(uint32_t, *(const float *)(Lwe + j * 64)) >> 23);
+            else if constexpr (WROW)
                 wsv[j & 1] = *(const v4f *)(Lw + j * 64);
             if (j + 2 < C::TN) {
                 awq[(j + 2) % 3] = frag(L + wo[0] + (j + 2) * 2048, L + wo[1] + (j + 2) * 2048);
@@ -890,7 +898,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
             for (int i = 0; i < C::TM; ++i) {
                 const int t = j * C::TM + i;
                 if constexpr (POW2)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], acc[i][j], 0, 0, 0, e8w, 0,
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bx[i], acc[i][j], 0, 0, 0, e8wj, 0,
                                                                                  e8[i]);
                 else
                     part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -1675,7 +1683,7 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
 }
 
 hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
-                             int64_t K, void *y, int out_fp32, hipStream_t stream)
+                             int64_t K, void *y, int out_fp32, int pow2, hipStream_t stream)
 {
     if (M == 0)
         return hipSuccess;
@@ -1692,10 +1700,14 @@ hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, co
     a.tiles_m = p.tiles_m;
     a.tiles_n = p.tiles_n;
     a.ksplit = 1;
+    // (POW2: the scales reach the matrix cores on the large-tile kernels; the general kernel's
+    // fp32 rescale applies them as it applies any other scales)
     if (p.kind == K_DMA256)
-        return run_dma_t<256, 256, 4, 2, false, false, true>(a, out_fp32 != 0, stream);
+        return pow2 ? run_dma_t<256, 256, 4, 2, false, true, true>(a, out_fp32 != 0, stream)
+                    : run_dma_t<256, 256, 4, 2, false, false, true>(a, out_fp32 != 0, stream);
     if (p.kind == K_DMA128)
-        return run_dma_t<128, 256, 2, 4, false, false, true>(a, out_fp32 != 0, stream);
+        return pow2 ? run_dma_t<128, 256, 2, 4, false, true, true>(a, out_fp32 != 0, stream)
+                    : run_dma_t<128, 256, 2, 4, false, false, true>(a, out_fp32 != 0, stream);
     const int grid = a.tiles_m * a.tiles_n;
     const dim3 block(2 * 2 * 64);
     if (out_fp32)

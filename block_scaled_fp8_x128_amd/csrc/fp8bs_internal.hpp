@@ -76,7 +76,7 @@ hipError_t launch_gemm(const void *xq, const float *xs, const void *wq, const fl
 // The product with per-row weight scales ws [N, K/128] (both operands in
 // 1x128 blocks along K): the weight gradient.
 hipError_t launch_gemm_1x128(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M, int64_t N,
-                             int64_t K, void *y, int out_fp32, hipStream_t stream);
+                             int64_t K, void *y, int out_fp32, int pow2, hipStream_t stream);
 // Y = fp8_block_gemm(quant_act_1x128(x), Wq, Ws) from bf16 x; the workspace
 // holds the quantized x (unless the shape runs fused) and the GEMM's own.
 size_t linear_workspace_size(int64_t M, int64_t N, int64_t K);

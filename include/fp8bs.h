@@ -319,6 +319,21 @@ FP8BS_API int fp8_block_gemm_1x128(const void *xq, const float *xs, const void *
                                    int64_t N, int64_t K, void *y, int out_dtype, void *stream);
 
 /*
+ * fp8_block_gemm_1x128_pow2 -- fp8_block_gemm_1x128 for operands quantized
+ * with power-of-2 scales (the article's closing section; scale_mode
+ * FP8BS_SCALE_POW2 of quant_act_1x128_t).  Arguments, layouts and errors are
+ * those of fp8_block_gemm_1x128, with the precondition of fp8_block_gemm_pow2
+ * on every xs and ws entry.  On the large-tile kernels both per-row scales go
+ * to the matrix cores' E8M0 operands (each lane passes the scale of the row of
+ * xq and of wq that it holds), so the MFMA accumulates 2^(ex + ew) * P
+ * directly, with no fp32 rescale pass; the results agree with
+ * fp8_block_gemm_1x128 on the same operands to within fp32 rounding of the
+ * accumulation order.
+ */
+FP8BS_API int fp8_block_gemm_1x128_pow2(const void *xq, const float *xs, const void *wq, const float *ws, int64_t M,
+                                        int64_t N, int64_t K, void *y, int out_dtype, void *stream);
+
+/*
  * fp8_block_grouped_gemm -- the MoE (mixture-of-experts) form of
  * fp8_block_gemm (article section "Real-world performance gains": the recipe
  * on Qwen3-30B, a mixture-of-experts model).

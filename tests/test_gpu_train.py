@@ -173,11 +173,19 @@ def _wgrad(fp8bs, orc, M, N, K, mode):
     assert torch.equal(dw16.view(torch.int16), dw32.to(torch.bfloat16).view(torch.int16))
     dw32b = fp8bs.fp8_block_gemm_1x128(dyq, dys, xq, xs, out_dtype=torch.float32)
     assert torch.equal(dw32.view(torch.int32), dw32b.view(torch.int32))
+    outs = [("dW fp32", dw32)]
+    if mode == 1:  # power-of-2 scales: the entry point that hands both scales to the matrix cores
+        p32 = fp8bs.fp8_block_gemm_1x128_pow2(dyq, dys, xq, xs, out_dtype=torch.float32)
+        p16 = fp8bs.fp8_block_gemm_1x128_pow2(dyq, dys, xq, xs, out_dtype=torch.bfloat16)
+        assert torch.equal(p16.view(torch.int16), p32.to(torch.bfloat16).view(torch.int16))
+        p32b = fp8bs.fp8_block_gemm_1x128_pow2(dyq, dys, xq, xs, out_dtype=torch.float32)
+        assert torch.equal(p32.view(torch.int32), p32b.view(torch.int32))
+        outs.append(("dW fp32 (pow2 entry)", p32))
     dyq_r, dys_r = orc.quant_act_1x128_t(dy, mode)
     xq_r, xs_r = orc.quant_act_1x128_t(x, mode)
     assert_bitexact("dyq", host(dyq), dyq_r)
     assert_bitexact("xq", host(xq), xq_r)
-    return dw32, dyq_r, dys_r, xq_r, xs_r
+    return outs, dyq_r, dys_r, xq_r, xs_r
 
 
 def test_mfma_dot_product_precision(fp8bs, orc):
@@ -223,10 +231,11 @@ def _abs_codes(q):
 def test_wgrad_parity_full_output(fp8bs, orc, shape, mode):
     M, N, K = shape
     say("wgrad tokens=%d N=%d K=%d mode=%d" % (M, N, K, mode))
-    dw32, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, mode)
+    outs, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, mode)
     ref = orc.gemm_1x128(dyq_r, dys_r, xq_r, xs_r)
     abs_sum = orc.gemm_1x128(_abs_codes(dyq_r), dys_r, _abs_codes(xq_r), xs_r)
-    gemm_gate_abs("dW fp32", host(dw32), ref, abs_sum)
+    for name, dw32 in outs:
+        gemm_gate_abs(name, host(dw32), ref, abs_sum)
 
 
 # the weight gradients of the 8B-shaped layers over 8192 tokens (persistent kernel, 256x256 tiles), and
@@ -234,15 +243,17 @@ def test_wgrad_parity_full_output(fp8bs, orc, shape, mode):
 WGRAD_LARGE = [(n, N, K, 8192) for n, N, K in DGRAD_LARGE] + [("tokens128_many_tiles", 8192, 4096, 128)]
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("case", WGRAD_LARGE, ids=lambda c: c[0])
-def test_wgrad_parity_full_size_sampled(fp8bs, orc, case):
+def test_wgrad_parity_full_size_sampled(fp8bs, orc, case, mode):
     name, N, K, M = case
-    say("wgrad %s tokens=%d N=%d K=%d" % (name, M, N, K))
-    dw32, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, 0)
+    say("wgrad %s tokens=%d N=%d K=%d mode=%d" % (name, M, N, K, mode))
+    outs, dyq_r, dys_r, xq_r, xs_r = _wgrad(fp8bs, orc, M, N, K, mode)
     rows, cols = sample_positions(N, K, 3000, seed=M + N + K)
     ref = orc.gemm_1x128_sampled(dyq_r, dys_r, xq_r, xs_r, rows, cols)
     abs_sum = orc.gemm_1x128_sampled(_abs_codes(dyq_r), dys_r, _abs_codes(xq_r), xs_r, rows, cols)
-    gemm_gate_abs("dW fp32 (sampled %d)" % rows.size, host(dw32)[rows, cols], ref, abs_sum)
+    for label, dw32 in outs:
+        gemm_gate_abs("%s (sampled %d)" % (label, rows.size), host(dw32)[rows, cols], ref, abs_sum)
 
 
 @pytest.mark.parametrize("shape", [(200, 256, 384), (77, 512, 1024), (1000, 384, 256), (300, 8192, 512)],
