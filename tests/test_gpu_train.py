@@ -256,23 +256,28 @@ def test_wgrad_parity_full_size_sampled(fp8bs, orc, case, mode):
         gemm_gate_abs("%s (sampled %d)" % (label, rows.size), host(dw32)[rows, cols], ref, abs_sum)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("shape", [(200, 256, 384), (77, 512, 1024), (1000, 384, 256), (300, 8192, 512)],
                          ids=lambda s: "%dx%dx%d" % s)
-def test_gemm_1x128_ragged_rows(fp8bs, orc, shape):
-    """fp8_block_gemm_1x128 straight from two 1x128-quantized operands, with row counts that
-    leave partial tiles (the persistent kernel where the width is a multiple of 256, the 128x128
-    kernel elsewhere); both operands carry the outlier recipe."""
+def test_gemm_1x128_ragged_rows(fp8bs, orc, shape, mode):
+    """fp8_block_gemm_1x128 (and with power-of-2 scales its _pow2 form) straight from two
+    1x128-quantized operands, with row counts that leave partial tiles (the persistent kernel
+    where the width is a multiple of 256, the 128x128 kernel elsewhere); both operands carry the
+    outlier recipe."""
     M, N, K = shape
-    say("fp8_block_gemm_1x128 M=%d N=%d K=%d" % (M, N, K))
+    say("fp8_block_gemm_1x128 M=%d N=%d K=%d mode=%d" % (M, N, K, mode))
     a = synth.activations(M, K, seed=synth.SEED, sub=synth.SUB_DY)
     b = synth.activations(N, K, seed=synth.SEED, sub=synth.SUB_X)
-    aq, as_ = fp8bs.quant_act_1x128(bf16_to_dev(a), 0)
-    bq, bs = fp8bs.quant_act_1x128(bf16_to_dev(b), 0)
-    y32 = fp8bs.fp8_block_gemm_1x128(aq, as_, bq, bs, out_dtype=torch.float32)
-    y16 = fp8bs.fp8_block_gemm_1x128(aq, as_, bq, bs, out_dtype=torch.bfloat16)
-    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
-    aq_r, as_r = orc.quant_act_1x128(a, 0)
-    bq_r, bs_r = orc.quant_act_1x128(b, 0)
+    aq, as_ = fp8bs.quant_act_1x128(bf16_to_dev(a), mode)
+    bq, bs = fp8bs.quant_act_1x128(bf16_to_dev(b), mode)
+    fns = [("Y fp32", fp8bs.fp8_block_gemm_1x128)] + ([("Y fp32 (pow2 entry)", fp8bs.fp8_block_gemm_1x128_pow2)]
+                                                      if mode else [])
+    aq_r, as_r = orc.quant_act_1x128(a, mode)
+    bq_r, bs_r = orc.quant_act_1x128(b, mode)
     ref = orc.gemm_1x128(aq_r, as_r, bq_r, bs_r)
     abs_sum = orc.gemm_1x128(_abs_codes(aq_r), as_r, _abs_codes(bq_r), bs_r)
-    gemm_gate_abs("Y fp32", host(y32), ref, abs_sum)
+    for label, fn in fns:
+        y32 = fn(aq, as_, bq, bs, out_dtype=torch.float32)
+        y16 = fn(aq, as_, bq, bs, out_dtype=torch.bfloat16)
+        assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+        gemm_gate_abs(label, host(y32), ref, abs_sum)
