@@ -152,18 +152,24 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
     }
     const __amdgpu_buffer_rsrc_t kr = attn_rsrc(a.kq + ((b * a.T) * a.Hkv + g) * AD, len * rowb);
     const __amdgpu_buffer_rsrc_t vr = attn_rsrc(a.vq + ((b * a.T) * a.Hkv + g) * AD, len * rowb);
-    const float *ksb = a.ks + (b * a.T) * a.Hkv + g;
-    const float *vsb = a.vs + (b * a.T) * a.Hkv + g;
+    // (the scales of tokens at or past len read as zeros, like the codes)
+    const __amdgpu_buffer_rsrc_t ksr = attn_rsrc(a.ks + (b * a.T) * a.Hkv + g, len * a.Hkv * 4);
+    const __amdgpu_buffer_rsrc_t vsr = attn_rsrc(a.vs + (b * a.T) * a.Hkv + g, len * a.Hkv * 4);
 
-    // Scores come out with heads down the MFMA's rows and the tile's 16
-    // tokens across its columns: lane (grp, n) holds heads 4 grp + r (r = 0
-    // .. 3) of token tb + n, so a head's max and sum over the tile are
-    // reductions within one 16-lane row (DPP), and each lane needs only its
-    // own token's scales.  The softmax state of head 4 grp + r is kept by
+    // Scores come out of the MFMAs with heads down the rows and the tile's 16
+    // tokens across the columns: lane (grp, n) holds heads 4 grp + r (r = 0
+    // .. 3) of token tb + n.  A transpose of the 4 x 4 blocks of 16-lane rows
+    // (three lane-row swaps) then gives lane (grp, n) heads 4 r + grp in its
+    // registers r < R, so that the G heads fill the rows of R = ceil(G / 4)
+    // registers instead of G of the 16 rows of four: a head's max and sum over
+    // the tile stay reductions within one 16-lane row (DPP), each lane needs
+    // only its own token's scales, and the softmax arithmetic runs on R
+    // registers, not four.  The softmax state of head 4 r + grp is kept by
     // every lane of its row (meaningful for heads < G) ...
-    float mh[4], lh[4];
+    constexpr int R = G > 4 ? 2 : 1;
+    float mh[R], lh[R];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < R; ++r) {
         mh[r] = -INFINITY;
         lh[r] = 0.0f;
     }
@@ -179,9 +185,9 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
 
     // The tile's operands, loaded one tile ahead: key bytes 32 grp .. + 31 of
     // token tb + n (B operand of the score MFMAs) with that token's key and
-    // value scales, and value dims d0 .. d0 + 7 of tokens tb + ts + 4 u.  Loads
-    // past the sequence's length read zeros (buffer range check); the scales
-    // are read only below t1.
+    // value scales, and value dims d0 .. d0 + 7 of tokens tb + ts + 4 u.  Codes
+    // and scales of tokens at or past the sequence's length read as zeros
+    // (buffer range check).
     struct TileIn {
         u32x4 k0, k1;
         u32x2 v[4];
@@ -195,9 +201,8 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             in.v[u] = __builtin_amdgcn_raw_buffer_load_b64(vr, (int)((tb + ts + 4 * u) * rowb) + d0, 0, 0);
-        const bool tok_ok = tb + n < t1;
-        in.ks = tok_ok ? ksb[(tb + n) * a.Hkv] : 0.0f;
-        in.vs = tok_ok ? vsb[(tb + n) * a.Hkv] : 0.0f;
+        in.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, (int)((tb + n) * a.Hkv * 4), 0, 0));
+        in.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, (int)((tb + n) * a.Hkv * 4), 0, 0));
         return in;
     };
     // (a tile at t1 or past it loads zeros and no scale)
@@ -212,23 +217,46 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[1], codes_to_bf16(cur.k0.z, cur.k0.w), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[2], codes_to_bf16(cur.k1.x, cur.k1.y), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[3], codes_to_bf16(cur.k1.z, cur.k1.w), acc, 0, 0, 0);
+        // 4 x 4 transpose of the row blocks (x[g][r] = row g of register r):
+        // swapping the upper halves of registers (0, 2) and (1, 3), then the
+        // odd rows of the new register 0 with the even rows of the new
+        // register 1, leaves row g of register r holding x[r][g], i.e. head
+        // 4 r + g of token tb + n
+        // (the elements go through plain scalars: this compiler's bit_cast of
+        // an indexed vector element reads element 0)
+        float st[R];
+        {
+            const float x0 = acc[0], x1 = acc[1], x2 = acc[2], x3 = acc[3];
+            const auto s02 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x0),
+                                                              __builtin_bit_cast(uint32_t, x2), false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x1),
+                                                              __builtin_bit_cast(uint32_t, x3), false, false);
+            const uint32_t n0 = s02[0], n1 = s13[0];
+            const auto s01 = __builtin_amdgcn_permlane16_swap(n0, n1, false, false);
+            const uint32_t t0 = s01[0], t1 = s01[1];
+            st[0] = __builtin_bit_cast(float, t0);
+            if constexpr (R > 1)
+                st[1] = __builtin_bit_cast(float, t1);
+        }
         const bool tok_ok = tb + n < t1;
         const float kscale = cur.ks * a.scale_log2; // scores in log2 units
-        float p[4], alpha[4];
+        float p[R], alpha[R];
+        bool moved = false; // a running max of this lane's heads changed
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float s = tok_ok ? acc[r] * kscale : -INFINITY;
+        for (int r = 0; r < R; ++r) {
+            const float s = tok_ok ? st[r] * kscale : -INFINITY;
             const float mt = row16_fmax(s);                       // finite: token tb is below t1
             const float mnew = mh[r] > mt ? mh[r] : mt;
             alpha[r] = __builtin_amdgcn_exp2f(mh[r] - mnew);      // 0 on the first tile
             p[r] = __builtin_amdgcn_exp2f(s - mnew);              // 0 for masked tokens
             lh[r] = lh[r] * alpha[r] + row16_fsum(p[r]);
             mh[r] = mnew;
+            moved = moved || (4 * r + grp < G && alpha[r] != 1.0f);
         }
         // p * vs of each (token, head) and the heads' rescale factors to the wave's LDS
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = 4 * grp + r;
+        for (int r = 0; r < R; ++r) {
+            const int h = 4 * r + grp;
             if (h < G) {
                 sh.pv[wave][n * G + h] = p[r] * cur.vs;
                 if (n == 0)
@@ -236,29 +264,28 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
             }
         }
         // ---- values: tokens ts + 4 u of the tile, dims d0 .. d0 + 7 ----
-        uint32_t vw[4][2];
+        // (LDS writes and reads of one wave complete in order.)  The output
+        // is rescaled only on tiles where some head's running max moved: a
+        // factor of exactly 1 leaves it unchanged, so skipping it changes no
+        // bit, and past the first tiles the max rarely moves
+        if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool ok = tb + ts + 4 * u < t1;
-            vw[u][0] = ok ? cur.v[u].x : 0u;
-            vw[u][1] = ok ? cur.v[u].y : 0u;
+            for (int h = 0; h < G; ++h) {
+                const float al = sh.alpha[wave][h];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[h][e] *= al;
+            }
         }
-        // (LDS writes and reads of one wave complete in order)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float al = sh.alpha[wave][h];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[h][e] *= al;
-        }
+        // (value codes of tokens at or past len read as zeros: their p is 0)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = ts + 4 * u;
             float v[8];
-            const f2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(vw[u][0], false);
-            const f2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8(vw[u][0], true);
-            const f2v v45 = __builtin_amdgcn_cvt_pk_f32_fp8(vw[u][1], false);
-            const f2v v67 = __builtin_amdgcn_cvt_pk_f32_fp8(vw[u][1], true);
+            const f2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].x, false);
+            const f2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].x, true);
+            const f2v v45 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].y, false);
+            const f2v v67 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].y, true);
             v[0] = v01.x, v[1] = v01.y, v[2] = v23.x, v[3] = v23.y;
             v[4] = v45.x, v[5] = v45.y, v[6] = v67.x, v[7] = v67.y;
 #pragma unroll
@@ -279,12 +306,12 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
             o[h][e] += __shfl_xor(o[h][e], 16);
             o[h][e] += __shfl_xor(o[h][e], 32);
         }
-    // head h's (max, sum) sit in row h / 4, register h % 4, of every lane of that row
+    // head h's (max, sum) sit in row h % 4, register h / 4, of every lane of that row
     float mrow[G], lrow[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        mrow[h] = __shfl(mh[h % 4], 16 * (h / 4));
-        lrow[h] = __shfl(lh[h % 4], 16 * (h / 4));
+        mrow[h] = __shfl(mh[h / 4], 16 * (h % 4));
+        lrow[h] = __shfl(lh[h / 4], 16 * (h % 4));
     }
     if (grp == 0) {
 #pragma unroll
