@@ -29,10 +29,11 @@
 //     rows and tokens across the columns, so per-head max and sum over a tile
 //     are DPP reductions within a 16-lane row; the key scale and
 //     sm_scale * log2(e) follow in fp32, and exp2 replaces exp;
-//   values: each lane owns 8 dimensions of every fourth token of the tile and
-//     accumulates p * vs * decode(v) for the G heads in fp32, p coming from the
-//     scores through the wave's LDS area; the four token groups' sums are
-//     added by two lane exchanges at the end.
+//   values: each lane owns 8 dimensions of every fourth token of the tile (4
+//     dimensions of every second token for G = 8) and accumulates
+//     p * vs * decode(v) for the G heads in fp32, p coming from the scores
+//     through the wave's LDS area; the token groups' sums are added by lane
+//     exchanges at the end.
 // With several splits per sequence a second kernel merges the splits' (max,
 // sum, output) in split order.  Every order is fixed, so results are
 // deterministic.
@@ -173,24 +174,30 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
         mh[r] = -INFINITY;
         lh[r] = 0.0f;
     }
-    // ... and the output partials: lane (ts = lane / 16, c = lane % 16) sums
-    // tokens ts, ts + 4, ts + 8, ts + 12 of each tile into dims 8 c .. 8 c + 7
-    const int ts = grp, d0 = 8 * n;
-    float o[G][8];
+    // ... and the output partials: the lanes form TG token groups of LPG
+    // lanes; lane (ts = lane / LPG, c = lane % LPG) sums tokens ts, ts + TG,
+    // ... of each tile into dims DPL c .. DPL c + DPL - 1 of all G heads.
+    // Four groups of 8 dims while G <= 4; two groups of 4 dims for G = 8,
+    // which halves the G x DPL accumulators (64 -> 32 registers), so that two
+    // workgroups of 8 waves still fit on a CU (at 4 x 8 the kernel needed
+    // more than the 128 registers a wave may hold at four waves per SIMD)
+    constexpr int TG = G > 4 ? 2 : 4, LPG = 64 / TG, DPL = 2 * TG, UPL = 16 / TG;
+    const int ts = lane / LPG, d0 = DPL * (lane % LPG);
+    float o[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < DPL; ++e)
             o[h][e] = 0.0f;
 
     // The tile's operands, loaded one tile ahead: key bytes 32 grp .. + 31 of
     // token tb + n (B operand of the score MFMAs) with that token's key and
-    // value scales, and value dims d0 .. d0 + 7 of tokens tb + ts + 4 u.  Codes
+    // value scales, and value dims d0 .. d0 + DPL - 1 of tokens tb + ts + TG u.  Codes
     // and scales of tokens at or past the sequence's length read as zeros
     // (buffer range check).
     struct TileIn {
         u32x4 k0, k1;
-        u32x2 v[4];
+        uint32_t v[UPL][DPL / 4];
         float ks, vs;
     };
     auto load_tile = [&](int64_t tb) {
@@ -199,8 +206,16 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
         in.k0 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 0, 0);
         in.k1 = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 16, 0, 0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            in.v[u] = __builtin_amdgcn_raw_buffer_load_b64(vr, (int)((tb + ts + 4 * u) * rowb) + d0, 0, 0);
+        for (int u = 0; u < UPL; ++u) {
+            const int off = (int)((tb + ts + TG * u) * rowb) + d0;
+            if constexpr (DPL == 8) {
+                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0);
+                in.v[u][0] = w.x;
+                in.v[u][DPL / 4 - 1] = w.y;
+            } else {
+                in.v[u][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, 0);
+            }
+        }
         in.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, (int)((tb + n) * a.Hkv * 4), 0, 0));
         in.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, (int)((tb + n) * a.Hkv * 4), 0, 0));
         return in;
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
                     sh.alpha[wave][h] = alpha[r];
             }
         }
-        // ---- values: tokens ts + 4 u of the tile, dims d0 .. d0 + 7 ----
+        // ---- values: tokens ts + TG u of the tile, dims d0 .. d0 + DPL - 1 ----
         // (LDS writes and reads of one wave complete in order.)  The output
         // is rescaled only on tiles where some head's running max moved: a
         // factor of exactly 1 leaves it unchanged, so skipping it changes no
@@ -273,38 +288,39 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
             for (int h = 0; h < G; ++h) {
                 const float al = sh.alpha[wave][h];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < DPL; ++e)
                     o[h][e] *= al;
             }
         }
         // (value codes of tokens at or past len read as zeros: their p is 0)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = ts + 4 * u;
-            float v[8];
-            const f2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].x, false);
-            const f2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].x, true);
-            const f2v v45 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].y, false);
-            const f2v v67 = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u].y, true);
-            v[0] = v01.x, v[1] = v01.y, v[2] = v23.x, v[3] = v23.y;
-            v[4] = v45.x, v[5] = v45.y, v[6] = v67.x, v[7] = v67.y;
+        for (int u = 0; u < UPL; ++u) {
+            const int t = ts + TG * u;
+            float v[DPL];
+#pragma unroll
+            for (int w = 0; w < DPL / 4; ++w) {
+                const f2v lo = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u][w], false);
+                const f2v hi = __builtin_amdgcn_cvt_pk_f32_fp8(cur.v[u][w], true);
+                v[4 * w] = lo.x, v[4 * w + 1] = lo.y, v[4 * w + 2] = hi.x, v[4 * w + 3] = hi.y;
+            }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const float pw = sh.pv[wave][t * G + h];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < DPL; ++e)
                     o[h][e] = __builtin_fmaf(pw, v[e], o[h][e]);
             }
         }
     }
 
-    // ---- sum the four token groups' partials; lanes of group 0 write ----
+    // ---- sum the token groups' partials; lanes of group 0 write ----
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o[h][e] += __shfl_xor(o[h][e], 16);
-            o[h][e] += __shfl_xor(o[h][e], 32);
+        for (int e = 0; e < DPL; ++e) {
+#pragma unroll
+            for (int m = LPG; m < 64; m *= 2)
+                o[h][e] += __shfl_xor(o[h][e], m);
         }
     // head h's (max, sum) sit in row h % 4, register h / 4, of every lane of that row
     float mrow[G], lrow[G];
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
         mrow[h] = __shfl(mh[h / 4], 16 * (h % 4));
         lrow[h] = __shfl(lh[h / 4], 16 * (h % 4));
     }
-    if (grp == 0) {
+    if (ts == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const int64_t bh = b * a.Hq + g * G + h;
@@ -324,25 +340,24 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
                     pp[1] = lrow[h];
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < DPL; ++e)
                     pp[2 + d0 + e] = o[h][e];
             } else {
-                float r[8];
+                float r[DPL];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < DPL; ++e)
                     r[e] = lrow[h] > 0.0f ? o[h][e] / lrow[h] : 0.0f;
-                if constexpr (OUT_F32) {
-                    float *op = (float *)a.out + bh * AD + d0;
-                    *(v4f *)op = v4f{r[0], r[1], r[2], r[3]};
-                    *(v4f *)(op + 4) = v4f{r[4], r[5], r[6], r[7]};
-                } else {
-                    const bf2v p0 = __builtin_convertvector(f2v{r[0], r[1]}, bf2v);
-                    const bf2v p1 = __builtin_convertvector(f2v{r[2], r[3]}, bf2v);
-                    const bf2v p2 = __builtin_convertvector(f2v{r[4], r[5]}, bf2v);
-                    const bf2v p3 = __builtin_convertvector(f2v{r[6], r[7]}, bf2v);
-                    *(u32x4 *)((__bf16 *)a.out + bh * AD + d0) =
-                        u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+#pragma unroll
+                for (int w = 0; w < DPL / 4; ++w) {
+                    if constexpr (OUT_F32) {
+                        *(v4f *)((float *)a.out + bh * AD + d0 + 4 * w) =
+                            v4f{r[4 * w], r[4 * w + 1], r[4 * w + 2], r[4 * w + 3]};
+                    } else {
+                        const bf2v p0 = __builtin_convertvector(f2v{r[4 * w], r[4 * w + 1]}, bf2v);
+                        const bf2v p1 = __builtin_convertvector(f2v{r[4 * w + 2], r[4 * w + 3]}, bf2v);
+                        *(u32x2 *)((__bf16 *)a.out + bh * AD + d0 + 4 * w) =
+                            u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+                    }
                 }
             }
         }
