@@ -424,7 +424,17 @@ __global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t 
 {
     __shared__ __attribute__((aligned(16))) uint8_t tl[128 * 256]; // the transposed bf16 tile
     const int64_t KB = K / 128, MB = M / 128;
-    const int64_t mb = blockIdx.x / KB, kb = blockIdx.x % KB;
+    // Tiles walk M fastest, over XCD-contiguous ranges: a tile writes 128-byte
+    // pieces of 128 rows of X^T's codes and one scale per row, and the tiles of
+    // one XCD then continue each other's rows through its L2 (against K-first
+    // tiles dealt round-robin: 11-24% faster from K = 14336 up, the same below)
+    int64_t mb, kb;
+    {
+        const int64_t n = MB * KB, x = blockIdx.x % 8, i = blockIdx.x / 8, qn = n / 8, r = n % 8;
+        const int64_t tile = x * qn + (x < r ? x : r) + i; // XCD x: [x qn + min(x, r), ...)
+        mb = tile % MB;
+        kb = tile / MB;
+    }
     const int t = threadIdx.x;
     const int rg = t >> 4, c = t & 15;
     const int64_t base = (mb * 128 + 8 * rg) * K + kb * 128 + c * 8;
