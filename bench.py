@@ -1163,7 +1163,7 @@ def summarize_trace(db, command, steps, warmup, out, workload="all"):
                                                                                       "csrc")))]
     title = "`bench.py` default run" if workload == "all" else "`bench.py --workload %s`" % workload
     lines = ["# rocprofv3 kernel trace: " + title, "",
-             "Command (on the MI355X box, from the repository root):", "", "    " + command, "",
+             "Command (on an MI355X, from the repository root):", "", "    " + command, "",
              "Sources at the time of the trace (sha256, first 16 hex digits):", ""]
     lines += ["- `%s`: %s" % (f, src_hash(os.path.join(ROOT, f))) for f in srcs]
     lines += ["- `bench.py`: %s" % src_hash(os.path.join(ROOT, "bench.py")), ""]
@@ -1215,7 +1215,7 @@ def summarize_counters(db, command, out):
     def ratio(a, b, scale=1.0):
         return None if a is None or not b else a / (b * scale)
 
-    lines = ["# rocprofv3 counters per kernel", "", "Command (on the MI355X box, from the repository root):", "",
+    lines = ["# rocprofv3 counters per kernel", "", "Command (on an MI355X, from the repository root):", "",
              "    " + command, "", "Counters: " + ", ".join("`%s`" % n for n in names), "",
              "Sources at the time of the run (sha256, first 16 hex digits):", ""]
     srcs = ["block_scaled_fp8_x128_amd/csrc/" + f for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp8_x128_amd",
