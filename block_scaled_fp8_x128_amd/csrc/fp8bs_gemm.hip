@@ -519,6 +519,19 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Cache policy of the persistent GEMM's output stores (bf16 Y, the quantizing
+// epilogue's codes): nontemporal (the `nt` bit).  A round of 32 tiles on one
+// XCD writes about 4 MiB of Y, the size of the XCD's L2, from which the other
+// units in flight still read their operand panels; streaming the output past
+// the caches keeps those panels resident.  Measured in the dense layer step
+// (M = 8192, a cache-evicting read between launches): step -1.2%, the GEMMs
+// 40.3% -> 40.9% of the FP8 peak; MoE gate+up -2.5%; with calls back to back,
+// dense gate+up -5.3% and MoE down -12.6%.  Split-K partial sums and the
+// quantizing epilogue's scale dwords keep the default policy: the reduction
+// reads the partials back at once, and the L2 combines the scattered dwords
+// into whole lines.
+constexpr int kOutPolicy = 2;
+
 // s_waitcnt lgkmcnt(0) with vmcnt / expcnt left alone.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
@@ -1025,7 +1038,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                         const u32x4 d = *(const u32x4 *)(epi_lds + r * C::EPI_RS + cc * 16);
                         const int m = wm * C::WM + i * 16 + r;
                         __builtin_amdgcn_raw_buffer_store_b128(d, qr, (int)((int64_t)m * N + wn * C::WN + cc * 16), 0,
-                                                               0);
+                                                               kOutPolicy);
                     }
                     const int64_t NB = N / 128;
                     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ys + g.row_begin * NB, rows * NB * 4);
@@ -1046,7 +1059,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                         const u32x4 d = *(const u32x4 *)(epi_lds + r * C::EPI_RS + cc * 16);
                         const int m = wm * C::WM + i * 16 + r;
                         const int n = wn * C::WN + c * C::EPI_CW + cc * 8;
-                        __builtin_amdgcn_raw_buffer_store_b128(d, yr, (int)(((int64_t)m * N + n) * 2), 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(d, yr, (int)(((int64_t)m * N + n) * 2), 0, kOutPolicy);
                     }
                 }
                 }
