@@ -60,7 +60,10 @@ __global__ __launch_bounds__(QA_THREADS) void quant_act_kernel(const u32x4 *__re
         bq.init(amax);
         const u32x2 codes = quant_chunk<MODE>(v[j], bq);
         if (b < nblocks) {
-            __builtin_nontemporal_store(codes, q + b * 16 + c);
+            // (default cache policy: the codes are the next GEMM's operand, which
+            // then reads them from the caches; the recalibration's quantizer,
+            // whose gigabytes of output would only evict, streams them instead)
+            q[b * 16 + c] = codes;
             if (c == 0)
                 s[b] = bq.s;
         }
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t 
         for (int j = 0; j < 8; ++j) {
             BlockQuant<MODE> bq;
             bq.init(amax_value(row16_max(chunk_max_mag(v[j]))));
-            __builtin_nontemporal_store(quant_chunk<MODE>(v[j], bq), (u32x2 *)(qr + base + j * K));
+            *(u32x2 *)(qr + base + j * K) = quant_chunk<MODE>(v[j], bq); // (cached: a GEMM operand next)
             if (c == 0)
                 sr[(mb * 128 + 8 * rg + j) * KB + kb] = bq.s;
         }
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(QW_THREADS) void quant_act_t_kernel(const uint16_t 
         bq.init(amax);
         const u32x2 codes = quant_chunk<MODE>(val, bq);
         const int64_t row = kb * 128 + p;
-        __builtin_nontemporal_store(codes, (u32x2 *)(q + row * M + mb * 128 + 8 * g));
+        *(u32x2 *)(q + row * M + mb * 128 + 8 * g) = codes; // (cached: the weight gradient's operand next)
         if (g == 0)
             s[row * MB + mb] = bq.s;
     }
