@@ -520,10 +520,11 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // Cache policy of the persistent GEMM's output stores (bf16 Y, the quantizing
-// epilogue's codes): nontemporal (the `nt` bit).  A round of 32 tiles on one
-// XCD writes about 4 MiB of Y, the size of the XCD's L2, from which the other
-// units in flight still read their operand panels; streaming the output past
-// the caches keeps those panels resident.  Measured in the dense layer step
+// epilogue's codes): nontemporal (the `nt` bit).  Y (67-235 MB per dense GEMM)
+// is never read back by the GEMM, while every XCD re-reads the weight panels
+// from the 256 MB last-level cache; streamed past the caches, the output no
+// longer evicts them.  (The traffic out of the L2s is unchanged, 657 MB per
+// launch: what changes is where it is served.)  Measured in the dense layer step
 // (M = 8192, a cache-evicting read between launches): step -1.2%, the GEMMs
 // 40.3% -> 40.9% of the FP8 peak; MoE gate+up -2.5%; with calls back to back,
 // dense gate+up -5.3% and MoE down -12.6%.  Split-K partial sums and the
