@@ -177,7 +177,7 @@ __global__ __launch_bounds__(SG_THREADS) void swiglu_quant_kernel(const uint16_t
         bq.init(amax);
         const u32x2 codes = quant_chunk<MODE>(h, bq);
         if (b < nblocks) {
-            __builtin_nontemporal_store(codes, q + (int64_t)b * 16 + c);
+            q[(int64_t)b * 16 + c] = codes; // (cached: the down projection's operand next)
             if (c == 0)
                 s[b] = bq.s;
         }
