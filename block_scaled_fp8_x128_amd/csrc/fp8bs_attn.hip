@@ -365,24 +365,50 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void kv_attn_decode_kernel(AttnArgs
 }
 
 // Merge of the splits of one (sequence, query head): one wave each, lane l
-// takes dims 2 l and 2 l + 1; the splits are added in split order.
+// takes dims 2 l and 2 l + 1; the splits are added in split order.  Lane s
+// loads split s's (max, sum) (splits <= 64, checked at launch), so those loads are in flight
+// together; the wave's max is a butterfly, lane s forms split s's factor and
+// every lane takes the factors in split order by lane reads, with the splits'
+// outputs loaded four splits ahead.  The sums are those of a lane that loads
+// and weighs the splits one after another, bit for bit.
 template <bool OUT_F32>
 __global__ __launch_bounds__(64) void kv_attn_combine_kernel(const float *part, int splits, void *out)
 {
     const int64_t bh = blockIdx.x;
     const int lane = threadIdx.x;
     const float *pp = part + bh * splits * (2 + AD);
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-        M = M > pp[s * (2 + AD)] ? M : pp[s * (2 + AD)];
+    const float ms = lane < splits ? pp[lane * (2 + AD)] : -INFINITY;
+    const float ls = lane < splits ? pp[lane * (2 + AD) + 1] : 0.0f;
+    float M = ms;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float t = __shfl_xor(M, o);
+        M = M > t ? M : t;
+    }
     float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
-            const float *q = pp + s * (2 + AD);
-            const float f = __builtin_amdgcn_exp2f(q[0] - M);
-            L = __builtin_fmaf(f, q[1], L);
-            o0 = __builtin_fmaf(f, q[2 + 2 * lane], o0);
-            o1 = __builtin_fmaf(f, q[3 + 2 * lane], o1);
+    if (M != -INFINITY) { // (uniform: every lane holds the wave's max)
+        const float fs = __builtin_amdgcn_exp2f(ms - M); // split `lane`'s factor (0 past the splits)
+        int s = 0;
+        for (; s + 4 <= splits; s += 4) {
+            float a[4], b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = pp[(s + j) * (2 + AD) + 2 + 2 * lane];
+                b[j] = pp[(s + j) * (2 + AD) + 3 + 2 * lane];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float f = __shfl(fs, s + j), l = __shfl(ls, s + j);
+                L = __builtin_fmaf(f, l, L);
+                o0 = __builtin_fmaf(f, a[j], o0);
+                o1 = __builtin_fmaf(f, b[j], o1);
+            }
+        }
+        for (; s < splits; ++s) {
+            const float f = __shfl(fs, s), l = __shfl(ls, s);
+            L = __builtin_fmaf(f, l, L);
+            o0 = __builtin_fmaf(f, pp[s * (2 + AD) + 2 + 2 * lane], o0);
+            o1 = __builtin_fmaf(f, pp[s * (2 + AD) + 3 + 2 * lane], o1);
         }
     }
     const float r0 = L > 0.0f ? o0 / L : 0.0f, r1 = L > 0.0f ? o1 / L : 0.0f;
@@ -423,6 +449,8 @@ static hipError_t run_attn(const AttnArgs &a, bool out_f32, hipStream_t stream)
 {
     const dim3 grid((unsigned)(a.B * ((a.Hkv + ATT_WAVES - 1) / ATT_WAVES)), (unsigned)a.splits),
         block(ATT_WAVES * 64);
+    if (a.splits > 64)
+        return hipErrorInvalidValue; // (attn_plan caps the splits at 64: one per lane of the merge)
     if (a.splits > 1) {
         hipError_t e = launch(kv_attn_decode_kernel<G, false, true>, grid, block, 0, stream, a);
         if (e != hipSuccess)
