@@ -61,6 +61,9 @@ CASES = [
     ("g1", 2, 200, 4, 4, [200, 63]),
     ("g2", 2, 129, 8, 4, [129, 128]),
     ("split_long", 8, 4096, 32, 8, [4096, 4000, 2049, 513, 1, 4095, 3000, 9999]),
+    # 80 sequences of one key/value head group: 7 splits per sequence, so the merge of the splits
+    # takes one group of four and a tail of three
+    ("splits7", 80, 2048, 4, 2, [2048 - 23 * i for i in range(80)]),
 ]
 
 
