@@ -796,10 +796,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 
     // Fragments and scale products of the step being computed.  Except for
     // the first step they are read from the step's LDS stage while the
-    // previous step's last two MFMA groups run.  W fragments rotate through
-    // a ring of three (the group being multiplied and the next two).
+    // previous step's last WD MFMA groups run.  W fragments rotate through a
+    // ring of WD + 1 (the group being multiplied and the next WD).  WD = 3
+    // where a step has 8 groups: each fragment read then has three groups
+    // of MFMAs to land instead of two, which made the 256x256 products
+    // 1.7-3.3% faster with bit-identical results.  Products with 4 groups a
+    // step (the 64- and 128-row tiles) showed no gain, and the fp32-output
+    // EXACT form with per-row weight scales would spill more; they keep
+    // WD = 2.
+    constexpr bool DEEP = C::TN >= 8 && !(WROW && OUT_F32 && !POW2);
+    constexpr int WD = DEEP ? 3 : 2, WR = WD + 1;
     v8i bx[C::TM];
-    v8i awq[3];
+    v8i awq[WR];
     float sc[C::TM];   // the step's scale product per row tile (POW2: the activation scale alone)
     float sw_cur = 1.f; // the step's weight scale (POW2)
     auto ws_of = [&](const TileGeo &g) {
@@ -823,22 +831,22 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
     static_assert(C::TN >= 4, "the W-fragment ring needs at least four groups per step");
 
     // One K block from registers.  Group j (TM MFMAs on one W fragment)
-    // reads the W fragment of group j + 2, so each LDS read has two groups of
+    // reads the W fragment of group j + WD, so each LDS read has WD groups of
     // MFMAs to land.  The rescale of MFMA tile t is issued after the MFMA of
     // tile t + 1, so the matrix core has the next product queued while the
-    // VALU applies the previous one.  Before group TN - 2 every wave waits for
-    // the next step's operands and for its own LDS reads (the last read of
-    // this stage was issued in group TN - 3), and passes the barrier: the next
-    // stage is then complete for all waves and no wave reads this stage any
-    // more, so the loads of a later step may refill it.  Those loads are
-    // spread over the MFMAs of groups TN - 2 and TN - 1 (issued in one block
-    // right after the barrier, where every wave of the CU is at the same
-    // point, they would leave the matrix cores idle while their addresses are
-    // formed).  Groups TN - 2 and TN - 1 also read the next step's first two
-    // W fragments and scales, and each MFMA of the last group frees its X
-    // fragment registers for the next step's.  (For the last step of a
-    // workgroup those reads fetch data that is never used; the barrier is
-    // uniform.)
+    // VALU applies the previous one.  Before group TN - WD every wave waits
+    // for the next step's operands and for its own LDS reads (the last read
+    // of this stage was issued in group TN - WD - 1), and passes the barrier:
+    // the next stage is then complete for all waves and no wave reads this
+    // stage any more, so the loads of a later step may refill it.  Those
+    // loads are spread over the MFMAs of the last WD groups (issued in one
+    // block right after the barrier, where every wave of the CU is at the
+    // same point, they would leave the matrix cores idle while their
+    // addresses are formed).  The last WD groups also read the next step's
+    // first WD W fragments and its scales, and each MFMA of the last group
+    // frees its X fragment registers for the next step's.  (For the last
+    // step of a workgroup those reads fetch data that is never used; the
+    // barrier is uniform.)
     auto compute = [&](int stage, int nstage, int wcur, bool full_wait, const CONST_AS float *swp, auto &&load_q)
                        __attribute__((always_inline)) {
         const uint8_t *L = lds + stage * C::STAGE_BYTES;
@@ -874,9 +882,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 e8wj = (int)(__builtin_bit_cast(uint32_t, *(const float *)(Lwe + j * 64)) >> 23);
             else if constexpr (WROW)
                 wsv[j & 1] = *(const v4f *)(Lw + j * 64);
-            if (j + 2 < C::TN) {
-                awq[(j + 2) % 3] = frag(L + wo[0] + (j + 2) * 2048, L + wo[1] + (j + 2) * 2048);
-            } else if (j + 2 == C::TN) {
+            if (j + WD < C::TN) {
+                awq[(j + WD) % WR] = frag(L + wo[0] + (j + WD) * 2048, L + wo[1] + (j + WD) * 2048);
+            } else if (j + WD == C::TN) {
                 // the next step's loads have landed; those of the steps after
                 // it (issued later) may still fly.  The count also covers
                 // stores, which may complete out of order with the loads: in
@@ -896,18 +904,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                     sw_next = *swp;
                 else
                     sw_next = 1.0f; // (the weight scale is applied per column)
-                awq[(j + 2) % 3] = frag(Ln + wo[0], Ln + wo[1]);
+                awq[(j + WD) % WR] = frag(Ln + wo[0], Ln + wo[1]);
 #pragma unroll
                 for (int i = 0; i < C::TM; ++i)
                     xs_next[i] = *(const float *)(Ln + so + i * 64);
             } else {
-                awq[(j + 2) % 3] = frag(Ln + wo[0] + 2048, Ln + wo[1] + 2048);
+                awq[(j + WD) % WR] = frag(Ln + wo[0] + (j + WD - C::TN) * 2048, Ln + wo[1] + (j + WD - C::TN) * 2048);
             }
             // the reads above stay ahead of this group's MFMAs (the machine
             // scheduler would otherwise sink them to where the registers they
             // fill are next used, shrinking the prefetch distance to zero)
             __builtin_amdgcn_sched_barrier(0);
-            const v8i aw = awq[j % 3];
+            const v8i aw = awq[j % WR];
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 const int t = j * C::TM + i;
@@ -921,23 +929,23 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
                 // one (whose product has had a full MFMA to land), and in the
                 // last group the next step's X fragment it freed; after the
                 // barrier, the next loads one or two per MFMA.  Only the last
-                // two groups, which carry the loads, are fenced per MFMA;
+                // WD groups, which carry the loads, are fenced per MFMA;
                 // elsewhere the scheduler may interleave MFMAs and rescales
                 // (about 1% faster than fencing every MFMA)
-                if (j + 2 >= C::TN)
+                if (j + WD >= C::TN)
                     __builtin_amdgcn_sched_barrier(0);
                 if (!POW2 && t > 0)
                     rescale(t - 1, part[(t - 1) & 1]);
                 if (last)
                     bx[i] = frag(Ln + xo[0] + i * 2048, Ln + xo[1] + i * 2048);
-                if (j + 2 >= C::TN) {
-                    const int slot_i = (j + 2 - C::TN) * C::TM + i;
+                if (j + WD >= C::TN) {
+                    const int slot_i = (j + WD - C::TN) * C::TM + i;
 #pragma unroll
                     for (int q = 0; q < C::DPW; ++q)
-                        if (q * 2 * C::TM / C::DPW == slot_i)
+                        if (q * WD * C::TM / C::DPW == slot_i)
                             load_q(q);
                 }
-                if (j + 2 >= C::TN)
+                if (j + WD >= C::TN)
                     __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -948,11 +956,17 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
         for (int i = 0; i < C::TM; ++i)
             sc[i] = POW2 ? xs_next[i] : xs_next[i] * sw_next;
         sw_cur = sw_next;
-        // the next step's groups 0 and 1 were read into slots TN % 3 and
-        // (TN + 1) % 3; move them to slots 0 and 1
-        const v8i n0 = awq[C::TN % 3], n1 = awq[(C::TN + 1) % 3];
-        awq[0] = n0;
-        awq[1] = n1;
+        // the next step's groups 0 .. WD - 1 were read into slots (TN + t) % WR;
+        // move them to slots 0 .. WD - 1 (nothing to move when TN % WR == 0)
+        if constexpr (C::TN % WR != 0) {
+            v8i nx[WD];
+#pragma unroll
+            for (int t = 0; t < WD; ++t)
+                nx[t] = awq[(C::TN + t) % WR];
+#pragma unroll
+            for (int t = 0; t < WD; ++t)
+                awq[t] = nx[t];
+        }
     };
 
     // Output of a finished work unit: buffer stores over the tile's own rows,
@@ -1126,8 +1140,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_dma_kernel(GemmArg
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
             bx[i] = frag(lds + xo[0] + i * 2048, lds + xo[1] + i * 2048);
-        awq[0] = frag(lds + wo[0], lds + wo[1]);
-        awq[1] = frag(lds + wo[0] + 2048, lds + wo[1] + 2048);
+#pragma unroll
+        for (int t = 0; t < WD; ++t)
+            awq[t] = frag(lds + wo[0] + t * 2048, lds + wo[1] + t * 2048);
     }
     bool has1 = has1_0;
     const CONST_AS float *wsp1 = wsp1_0;
