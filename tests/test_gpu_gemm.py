@@ -92,6 +92,27 @@ def test_gemm_parity_full_output(fp8bs, orc, shape, mode):
         float((y32 - yb).abs().max() / yb.pow(2).mean().sqrt()))
 
 
+# The 256x256 persistent kernel with units of one to three K blocks: every step, or every other one,
+# ends a tile while the next tile's first W fragments are already being read (three MFMA groups
+# ahead); a ragged last row tile (M = 4000) and 17 column tiles (N = 4352).  Every output is checked.
+SHORT_K_256 = [(4096, 4096, 128), (4000, 4096, 384), (4096, 4352, 256)]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", SHORT_K_256, ids=lambda s: "%dx%dx%d" % s)
+def test_gemm_256x256_short_k_full_output(fp8bs, orc, shape, mode):
+    M, N, K = shape
+    say("fp8_block_gemm (256x256 tiles, short K) M=%d N=%d K=%d mode=%d" % (M, N, K, mode))
+    x, w, xd, wd, xq, xs, wq, ws, y32, y16, ((xq_r, xs_r), (wq_r, ws_r)) = _run_pair(fp8bs, orc, M, N, K, mode)
+    assert_bitexact("xq", host(xq), xq_r)
+    assert_bitexact("wq", host(wq), wq_r)
+    ref = orc.gemm_full(xq_r, xs_r, wq_r, ws_r)
+    gemm_gate("Y fp32", host(y32), ref)
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    if mode == 1:
+        gemm_gate("Y fp32 (pow2 entry)", host(_pow2_outputs(fp8bs.fp8_block_gemm_pow2, xq, xs, wq, ws)), ref)
+
+
 def test_gemm_integer_special_case(fp8bs):
     """Codes of small integers with unit scales: the product is an exact integer
     matmul, which fp32 accumulation reproduces exactly at this size."""
