@@ -51,6 +51,21 @@ def test_pair_out():
             fp8bs._pair_out(bad, 5, 384, CPU)
 
 
+def test_out_error_names_the_buffer():
+    good = torch.empty((5, 384), dtype=torch.uint8)
+    with pytest.raises(ValueError, match=r"out\[1\] \(xs\) must have shape \(5, 3\)"):
+        fp8bs._pair_out((good, torch.empty((5, 2), dtype=torch.float32)), 5, 384, CPU)
+    with pytest.raises(ValueError, match=r"out\[0\] \(hq\) must have dtype"):
+        fp8bs._pair_out((torch.empty((5, 384), dtype=torch.int8), torch.empty((5, 3))), 5, 384, CPU, "hq", "hs")
+    with pytest.raises(ValueError, match=r"^t must be contiguous$"):
+        fp8bs._out(torch.empty((256, 4), dtype=torch.uint8).t(), (4, 256), fp8bs._CODE_DTYPES, CPU, "t")
+
+
+def test_pointer_arguments_are_plain_ints():
+    t = torch.empty(16, dtype=torch.uint8)
+    assert fp8bs._ptr(t) == t.data_ptr() and fp8bs._ptr(None) is None
+
+
 def test_w_and_dual_outs():
     w = torch.empty((256, 384), dtype=torch.bfloat16)
     wq, ws = fp8bs._w_out(None, w)
