@@ -927,12 +927,33 @@ def row_tiny(fp8bs, dev, steps, warmup, cpu):
         maybe(t, "layer", layer)
         maybe(t, "gemm", lambda: fp8bs.fp8_block_gemm(xq, xs, wq, ws, out=y))
     torch.cuda.synchronize()
+    # the same three calls captured once in a HIP graph and replayed: one launch per layer, no
+    # per-call host work (the library issues kernel launches only, so the calls capture as they are)
+    def layer():
+        fp8bs.quant_act_1x128(x, 0, out=(xq, xs))
+        fp8bs.quant_w_128x128(w, 0, out=(wq, ws))
+        fp8bs.fp8_block_gemm(xq, xs, wq, ws, out=y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    torch.cuda.synchronize()
+    for r in range(warmup + reps):
+        maybe(timer if r >= warmup else None, "layer_graph", graph.replay)
+    torch.cuda.synchronize()
     lm, lmin = timer.spread("layer")
     gm, gmin = timer.spread("gemm")
+    grm, grmin = timer.spread("layer_graph")
     out = {"config": "X [256,512], W [512,512], seed 0, EXACT: quant_act_1x128 + quant_w_128x128 + fp8_block_gemm "
-                     "(bf16 out), three launches on one stream, %d timed repetitions" % reps,
+                     "(bf16 out), three launches on one stream, %d timed repetitions; layer_graph: the three "
+                     "calls captured in one HIP graph, one replay per event pair" % reps,
            "latency_us": {"layer_median": round(lm * 1e3, 2), "layer_min": round(lmin * 1e3, 2),
-                          "gemm_median": round(gm * 1e3, 2), "gemm_min": round(gmin * 1e3, 2)},
+                          "gemm_median": round(gm * 1e3, 2), "gemm_min": round(gmin * 1e3, 2),
+                          "layer_graph_median": round(grm * 1e3, 2), "layer_graph_min": round(grmin * 1e3, 2)},
            "flops": 2.0 * M * N * K}
     if cpu:
         out["cpu_baseline"] = cpu_tiny()
